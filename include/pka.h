@@ -1,0 +1,176 @@
+/*
+ * pka.h - paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Three operations form one serving step
+ * of a paged KV cache:
+ *
+ *   pka_store_kv            new K/V rows -> their slots in the K/V pools
+ *   pka_paged_attn_prefill  causal extend (chunked) prefill on top of a cached prefix
+ *   pka_paged_attn_decode   batched GQA decode, split over the key axis, then merged
+ *
+ * The pages this follows describe a pool shared by all requests whose
+ * allocation unit is a page of page_size tokens (default 1) ["Mini-SGLang
+ * deployment guide" (dpshk.com), section 6.2 "Page Size" and section 6.5 "Radix
+ * Cache"]; attention that reads the pool's history together with the freshly
+ * computed K/V, finding each request's tokens through a page table and position
+ * metadata ["miniSGLang intro blog" (0539edu.com), section 1.3 "forward
+ * computation"]; prefill and decode served by different kernels, with chunked
+ * prefill extending a cached prefix [deployment guide, sections 6.1 and 6.3;
+ * "Mini-SGLang: Efficient Inference Engine in a Nutshell", section on integrated
+ * high-performance kernels].
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ * Data types. bf16 tensors are passed as `void*` (16-bit bf16 bit patterns);
+ *   index arrays are int32; the softmax scale is a float.
+ * Memory. Every pointer argument is a device pointer to contiguous row-major
+ *   memory owned by the caller. The library allocates and frees nothing.
+ * Pools. k_pool and v_pool are each [num_pages * page_size, Hkv, D] bf16: slot-major,
+ *   one slot holds one token's K (or V) for all Hkv kv heads, and page p owns
+ *   slots p*page_size .. p*page_size + page_size - 1.
+ * Page table. page_table[b * page_table_stride + n] is the page holding logical
+ *   tokens n*P .. n*P+P-1 of request b. Token j of request b therefore lives in
+ *   slot page_table[b*stride + j/P]*P + j%P. Entries past ceil(L_b/P) are never read.
+ * GQA. q head h reads kv head h / (Hq / Hkv) (contiguous groups).
+ * Streams. `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *   enqueues work: it never waits for the device and never copies device data to
+ *   the host, so a sequence of calls can be captured into a HIP graph.
+ * Order. Attention reads the new tokens' K/V from the pools, so store the step's
+ *   new tokens with pka_store_kv first, on the same stream.
+ * Errors. Host-side arguments (pointers, sizes, geometry) are checked before
+ *   anything is enqueued; on error the call returns a negative status and enqueues
+ *   nothing. A failed launch returns PKA_E_HIP. Device-resident metadata (page ids,
+ *   slots, lengths) is not read by the host. A page id or slot outside the pool is
+ *   never dereferenced: such a key is skipped (store) or treated as absent
+ *   (attention), so the result is unspecified but no out-of-bounds access occurs.
+ * Aliasing. out must not overlap q, the pools or the workspace; new K/V must not
+ *   overlap the pools. Requests may share read-only prefix pages, but the slots the
+ *   step writes must belong to one request only and must be pairwise distinct.
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PKA_OK 0
+#define PKA_E_NULLPTR (-1)     /* a required pointer is NULL */
+#define PKA_E_SHAPE (-2)       /* a size or geometry value is invalid */
+#define PKA_E_UNSUPPORTED (-3) /* valid, but not supported by these kernels */
+#define PKA_E_WORKSPACE (-4)   /* workspace missing or smaller than required */
+#define PKA_E_HIP (-5)         /* the HIP runtime reported an error */
+
+/* Pool and head geometry, shared by all calls.
+ *   num_q_heads  Hq >= 1, a multiple of num_kv_heads
+ *   num_kv_heads Hkv >= 1
+ *   head_dim     D; attention supports D == 128, store_kv any D with D % 8 == 0
+ *   page_size    P >= 1 tokens per page
+ *   num_pages    pages in each pool; the pools hold num_pages * P slots      */
+typedef struct pka_geom {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int64_t num_pages;
+} pka_geom;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pka_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* pka_status_string(int status);
+
+/*
+ * pka_store_kv - write the step's new K/V rows into their pool slots.
+ *
+ * The new keys and values of a step join the pool's history before attention
+ * reads them [miniSGLang intro blog, section 1.3]; a slot is one token of one
+ * page [deployment guide, section 6.2].
+ *
+ *   k_new, v_new  [num_tokens, Hkv, D] bf16 (device)
+ *   out_loc       [num_tokens] int32 slot ids (device); slot out_loc[t] receives
+ *                 row t. Slots must be pairwise distinct; a slot outside
+ *                 [0, num_pages*P) is skipped.
+ *   k_pool, v_pool  the pools (device), updated in place
+ * The copy is bit-exact. num_tokens == 0 is a no-op returning PKA_OK.
+ */
+int pka_store_kv(const pka_geom* geom, const void* k_new, const void* v_new,
+                 const int32_t* out_loc, int32_t num_tokens, void* k_pool, void* v_pool,
+                 void* stream);
+
+/*
+ * pka_paged_attn_decode - one new token per request attends to all its keys.
+ *
+ * Batched decode over the paged pool [deployment guide, sections 6.2-6.4]. For
+ * request b, q head h and kv head g = h / (Hq/Hkv):
+ *   out[b,h,:] = softmax_j(scale * q[b,h,:] . K_b[j,g,:]) . V_b[j,g,:], j < L_b,
+ * where K_b[j] is the pool row of token j of request b. L_b = seq_lens[b] counts
+ * the new token, whose K/V must already be stored.
+ *
+ *   q             [batch, Hq, D] bf16 (device)
+ *   page_table    [batch, page_table_stride] int32 page ids (device)
+ *   seq_lens      [batch] int32, 1 <= L_b <= max_seq_len (device)
+ *   max_seq_len   host-known upper bound of seq_lens; sets the split plan
+ *   scale         softmax scale (usually 1/sqrt(D))
+ *   out           [batch, Hq, D] bf16 (device)
+ *   workspace     device scratch of at least
+ *                 pka_decode_workspace_bytes(geom, batch, max_seq_len) bytes
+ *                 (may be NULL when that size is 0). Contents on entry are ignored.
+ * Supported: D == 128, Hq/Hkv <= 16. batch == 0 is a no-op.
+ */
+int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* page_table,
+                          int32_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                          int32_t max_seq_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pka_paged_attn_decode needs for this geometry and plan. */
+size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t max_seq_len);
+
+/*
+ * pka_paged_attn_prefill - causal extend prefill on top of a cached prefix.
+ *
+ * Chunked prefill [deployment guide, section 6.1] over a prefix reused from the
+ * radix cache [deployment guide, section 6.5]. Request b has p_b = prefix_lens[b]
+ * cached tokens and e_b = extend_lens[b] new tokens; L_b = seq_lens[b] = p_b + e_b.
+ * New token i of request b (q row cu_extend[b] + i) sits at absolute position
+ * p_b + i and attends to keys 0 .. p_b + i of its request (causal, aligned to the
+ * end of the sequence). All L_b keys, including the new ones, are read from the
+ * pools, so the new tokens must be stored first.
+ *
+ *   q             [num_tokens, Hq, D] bf16 (device); requests packed in batch order
+ *   page_table    [batch, page_table_stride] int32 page ids (device)
+ *   seq_lens, prefix_lens, extend_lens  [batch] int32 (device)
+ *   cu_extend     [batch + 1] int32 exclusive prefix sums of extend_lens (device)
+ *   num_tokens    host-known sum of extend_lens
+ *   max_extend    host-known upper bound of extend_lens
+ *   max_seq_len   host-known upper bound of seq_lens
+ *   out           [num_tokens, Hq, D] bf16 (device)
+ *   workspace     device scratch of at least
+ *                 pka_prefill_workspace_bytes(geom, batch, num_tokens, max_extend) bytes
+ * Supported: D == 128. Requests with e_b == 0 produce no rows. batch == 0 or
+ * num_tokens == 0 is a no-op.
+ */
+int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* page_table,
+                           int32_t page_table_stride, const int32_t* seq_lens,
+                           const int32_t* prefix_lens, const int32_t* extend_lens,
+                           const int32_t* cu_extend, int32_t batch, int32_t num_tokens,
+                           int32_t max_extend, int32_t max_seq_len, float scale, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pka_paged_attn_prefill needs (0 for the current kernels). */
+size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,
+                                   int32_t max_extend);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKA_H */

@@ -1,0 +1,80 @@
+// Launchers of the gfx950 kernels (internal C++ interface between the C ABI and
+// the kernels). Arguments are already validated by the caller; each launcher only
+// enqueues work on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pka {
+
+struct StoreArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* out_loc;
+  int32_t num_tokens;
+  int32_t row_chunks;  // 16-byte chunks per pool row (Hkv * D * 2 / 16)
+  int64_t num_slots;
+  void* k_pool;
+  void* v_pool;
+};
+hipError_t launch_store_kv(const StoreArgs& a, hipStream_t stream);
+
+// Split plan of the decode kernel: keys of request b are cut into chunks of
+// `chunk` tokens; chunk s of request b is one work unit.
+struct DecodePlan {
+  int32_t chunk;
+  int32_t num_splits;  // ceil(max_seq_len / chunk)
+};
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, const DecodePlan& plan);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* out;
+  void* workspace;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t pt_stride;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  const int32_t* cu_extend;
+  void* out;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t pt_stride;
+  int32_t batch;
+  int32_t num_tokens;
+  int32_t max_extend;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+inline int32_t page_shift_of(int32_t page_size) {
+  if (page_size <= 0 || (page_size & (page_size - 1)) != 0) return -1;
+  int32_t s = 0;
+  while ((1 << s) < page_size) ++s;
+  return s;
+}
+
+}  // namespace pka
