@@ -1,0 +1,300 @@
+"""Benchmark of the paged KV-cache attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+Prints ONE JSON line. The headline workload is the offline-style decode batch
+(Qwen3-0.6B heads 16q/8kv, d=128, bf16, batch 256, context lengths uniform in
+[200, 2048], page size 1, slots scattered over a 2^20-slot pool). One step is the
+whole decode step of the path: store_kv of the 256 new tokens, then the split
+decode kernel and its merge pass. `value` is the step's algorithmic HBM bytes
+(K+V of every attended token, q, out, page-table entries and seq_lens, plus the
+store's reads and writes) divided by the step's time, with inputs resident in
+HBM and the caches flushed (a 1 GiB write) before every timed step.
+
+The other workloads (chunked prefill over cached prefixes, the tensor-parallel
+mixed step, long-context decode, tiny decode) are timed the same way and reported
+under "parts": decode in GB/s against the 8 TB/s HBM peak, prefill in TFLOP/s
+(4*D flops per unmasked (query, key) pair per q head) against the 2.5 PFLOP/s
+dense bf16 MFMA peak.
+
+Times come from HIP events recorded on the stream the kernels run on (torch's
+current stream, which the binding passes to every call). The oracle (float64,
+numpy, one BLAS thread) is timed on the host over the full decode batch as
+"cpu_baseline".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+METRIC = "decode attn HBM GB/s (% peak) + prefill attn TFLOP/s (% MFMA peak), 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b256_traffic.json")
+
+
+def decode_bytes(part, step):
+    """Algorithmic bytes of one decode call: K+V rows of every attended token, q, out,
+    page-table entries and seq_lens."""
+    d, hkv, hq = step.head_dim, step.num_kv_heads, step.num_q_heads
+    seq = part.seq_lens.astype(np.int64)
+    kv = int(seq.sum()) * hkv * d * 2 * 2
+    qo = 2 * part.batch * hq * d * 2
+    pt = 4 * int((-(-seq // step.page_size)).sum()) + 4 * part.batch
+    return kv + qo + pt
+
+
+def prefill_flops(part, step):
+    """4*D flops per unmasked (query, key) pair per q head."""
+    p = part.prefix_lens.astype(np.int64)
+    e = part.extend_lens.astype(np.int64)
+    pairs = int((e * p + e * (e + 1) // 2).sum())
+    return 4 * step.head_dim * step.num_q_heads * pairs
+
+
+def prefill_bytes(part, step):
+    d, hkv, hq = step.head_dim, step.num_kv_heads, step.num_q_heads
+    seq = part.seq_lens.astype(np.int64)
+    return int(seq.sum()) * hkv * d * 4 + 2 * part.num_tokens * hq * d * 2
+
+
+def store_bytes(step):
+    rows = step.out_loc.size
+    return rows * step.num_kv_heads * step.head_dim * 2 * 2 * 2 + 4 * rows
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_attention_25_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Device-resident metadata and closures for one workload step."""
+
+    def __init__(self, step):
+        import torch
+        import paged_kv_attention_25_amd as pka
+        self.step = step
+        self.pka = pka
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        self.out_loc = i32(step.out_loc)
+        self.meta = []
+        for part in step.parts:
+            m = dict(pt=i32(part.page_table), seq=i32(part.seq_lens))
+            if part.kind == "decode":
+                need = pka.decode_workspace_bytes(step.num_q_heads, step.num_kv_heads,
+                                                  step.head_dim, step.page_size, step.num_pages,
+                                                  part.batch, part.max_seq_len)
+                m["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            else:
+                m.update(pre=i32(part.prefix_lens), ext=i32(part.extend_lens),
+                         cu=i32(part.cu_extend))
+            m["out"] = torch.empty_like(part.q)
+            self.meta.append(m)
+
+    def store(self):
+        s = self.step
+        self.pka.store_kv(s.k_new, s.v_new, self.out_loc, s.k_pool, s.v_pool, s.page_size)
+
+    def attend(self, i):
+        s, part, m = self.step, self.step.parts[i], self.meta[i]
+        if part.kind == "decode":
+            self.pka.paged_attn_decode(part.q, s.k_pool, s.v_pool, m["pt"], m["seq"],
+                                       part.max_seq_len, s.page_size, s.scale, out=m["out"],
+                                       workspace=m["ws"])
+        else:
+            self.pka.paged_attn_prefill(part.q, s.k_pool, s.v_pool, m["pt"], m["seq"], m["pre"],
+                                        m["ext"], m["cu"], part.max_extend, part.max_seq_len,
+                                        s.page_size, s.scale, out=m["out"])
+
+
+def time_step(runner, steps, warmup, flush, cold=True):
+    """Run warmup steps, then `steps` timed steps. Each timed step records HIP events
+    between its calls (store, then each attention part) on the current stream; a cache
+    flush runs before each timed step, outside the events. Returns per-segment mean ms,
+    total mean ms and the wall time of the bracketed region."""
+    import torch
+    nparts = len(runner.step.parts)
+    for _ in range(warmup):
+        runner.store()
+        for i in range(nparts):
+            runner.attend(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nparts + 2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if cold:
+            flush()
+        e = evs[k]
+        e[0].record()
+        runner.store()
+        e[1].record()
+        for i in range(nparts):
+            runner.attend(i)
+            e[i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.zeros(nparts + 1)
+    for e in evs:
+        for j in range(nparts + 1):
+            seg[j] += e[j].elapsed_time(e[j + 1])
+    seg /= steps
+    return seg, float(seg.sum()), wall
+
+
+def cpu_baseline(step, min_seconds=10.0):
+    """The oracle timed on the host (one BLAS thread) over the whole decode batch,
+    repeated until at least `min_seconds` have passed."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    part = step.parts[0]
+    kp = step.k_pool.cpu().numpy().view(np.uint16)
+    vp = step.v_pool.cpu().numpy().view(np.uint16)
+    q = part.q.cpu().numpy().view(np.uint16)
+    reps = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode_ref(q, kp, vp, part.page_table, part.seq_lens, step.page_size,
+                              step.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    gbs = decode_bytes(part, step) * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full decode_b256 batch (256 requests), {reps} pass(es) in {el:.1f} s, "
+                      "float64 numpy, one BLAS thread, same byte accounting as value"}
+
+
+def traffic_for(kernel_hash):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_hash:
+        return None      # counters were taken on an older kernel
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--hot", action="store_true", help="also report hot-cache times")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attention_25_amd as pka
+    from paged_kv_attention_25_amd import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pka.lib()
+    torch.cuda.set_device(0)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: flush_buf.fill_(1)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # --- headline: decode_b256 ------------------------------------------------------
+    log("decode_b256: generating inputs")
+    step = W.decode_b256(device="cuda", fill="zero")
+    run = Runner(step)
+    part = step.parts[0]
+    torch.cuda.synchronize()
+    seg, total_ms, wall = time_step(run, args.steps, args.warmup, flush)
+    dec_bytes = decode_bytes(part, step)
+    st_bytes = store_bytes(step)
+    value = (dec_bytes + st_bytes) / (total_ms * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (seg[1] * 1e-3) / 1e9
+    log(f"decode_b256: step {total_ms*1e3:.1f} us (store {seg[0]*1e3:.1f}, decode "
+        f"{seg[1]*1e3:.1f}); decode {dec_gbs:.0f} GB/s")
+    khash = source_hash("decode.hip", "pka_device.h")
+    roofline = {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
+                "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(khash),
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(seg[1] * 1e3, 2)}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v; lengths and page permutations seeded)",
+        "config": {"workload": "decode_b256: Qwen3-0.6B heads 16q/8kv, d=128, batch 256, "
+                               "context U[200,2048], page_size 1, 2^20-slot pool; "
+                               "step = store_kv(256) + split decode + merge",
+                   "batch": part.batch, "sum_context": int(part.seq_lens.sum()),
+                   "timing": "HIP events on the launch stream, caches flushed before each step",
+                   "wall_s_timed_region_incl_flush": round(wall, 4)},
+        "roofline": roofline,
+    }
+    if args.hot:
+        seg_h, tot_h, _ = time_step(run, args.steps, 0, flush, cold=False)
+        result["config"]["hot_cache_decode_GBs"] = round(dec_bytes / (seg_h[1] * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on decode_b256")
+        result["cpu_baseline"] = cpu_baseline(step)
+    else:
+        result["cpu_baseline"] = None
+    del run, step
+    torch.cuda.empty_cache()
+
+    parts = {}
+    if not args.quick:
+        for name in ("chunked_prefill", "tp4_mixed", "long_decode", "tiny_decode"):
+            log(f"{name}: generating inputs")
+            st = W.WORKLOADS[name](device="cuda", fill="zero")
+            r = Runner(st)
+            torch.cuda.synchronize()
+            seg, tot, _ = time_step(r, args.steps, args.warmup, flush)
+            rec = {"step_us": round(tot * 1e3, 2), "store_us": round(seg[0] * 1e3, 2),
+                   "store_GBs": round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1)}
+            for i, p in enumerate(st.parts):
+                us = seg[i + 1] * 1e3
+                if p.kind == "decode":
+                    gbs = decode_bytes(p, st) / (us * 1e-6) / 1e9
+                    rec["decode_us"] = round(us, 2)
+                    rec["decode_GBs"] = round(gbs, 1)
+                    rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+                else:
+                    tf = prefill_flops(p, st) / (us * 1e-6) / 1e12
+                    rec["prefill_us"] = round(us, 2)
+                    rec["prefill_TFLOPs"] = round(tf, 1)
+                    rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+                    rec["prefill_flops"] = prefill_flops(p, st)
+            log(f"{name}: {rec}")
+            parts[name] = rec
+            del r, st
+            torch.cuda.empty_cache()
+        cp = parts["chunked_prefill"]
+        result["prefill"] = {"workload": "chunked_prefill: Qwen3-14B heads 40q/8kv, 32 requests, "
+                                         "prefixes U[0,4096], 8192 new tokens, page_size 16",
+                             "value": cp["prefill_TFLOPs"], "unit": "TFLOP/s",
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "frac": cp["prefill_frac_mfma"]}
+    result["parts"] = parts
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
