@@ -9,7 +9,7 @@ whole decode step of the path: store_kv of the 256 new tokens, then the split
 decode kernel and its merge pass. `value` is the step's algorithmic HBM bytes
 (K+V of every attended token, q, out, page-table entries and seq_lens, plus the
 store's reads and writes) divided by the step's time, with inputs resident in
-HBM and the caches flushed (a 1 GiB write) before every timed step.
+HBM and the caches flushed (a 1 GiB read) before every timed step.
 
 The other workloads (chunked prefill over cached prefixes, the tensor-parallel
 mixed step, long-context decode, tiny decode) are timed the same way and reported
@@ -97,7 +97,7 @@ class Runner:
                 need = pka.decode_workspace_bytes(step.num_q_heads, step.num_kv_heads,
                                                   step.head_dim, step.page_size, step.num_pages,
                                                   part.batch, part.max_seq_len)
-                m["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+                m["ws"] = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
             else:
                 m.update(pre=i32(part.prefix_lens), ext=i32(part.extend_lens),
                          cu=i32(part.cu_extend))
@@ -211,8 +211,12 @@ def main():
         sys.exit(1)
     pka.lib()
     torch.cuda.set_device(0)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    flush = lambda: flush_buf.fill_(1)
+    # Cold caches without unrelated write-back: reading 1 GiB evicts the 4 MB L2s and
+    # the 256 MB Infinity Cache with clean lines (a write-based flush would leave
+    # dirty lines whose write-back would be charged to the timed kernels).
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
+    flush = lambda: torch.sum(flush_buf, dim=0, out=flush_sink)
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)

@@ -41,9 +41,10 @@
  * Errors. Host-side arguments (pointers, sizes, geometry) are checked before
  *   anything is enqueued; on error the call returns a negative status and enqueues
  *   nothing. A failed launch returns PKA_E_HIP. Device-resident metadata (page ids,
- *   slots, lengths) is not read by the host. A page id or slot outside the pool is
- *   never dereferenced: such a key is skipped (store) or treated as absent
- *   (attention), so the result is unspecified but no out-of-bounds access occurs.
+ *   slots, lengths) is not read by the host. A page id or slot outside the pool, or
+ *   a page-table index past the row, is never dereferenced: store_kv skips such a
+ *   row, attention reads a slot inside the pool instead, so the affected results are
+ *   unspecified but no out-of-bounds access occurs.
  * Aliasing. out must not overlap q, the pools or the workspace; new K/V must not
  *   overlap the pools. Requests may share read-only prefix pages, but the slots the
  *   step writes must belong to one request only and must be pairwise distinct.
@@ -120,9 +121,11 @@ int pka_store_kv(const pka_geom* geom, const void* k_new, const void* v_new,
  *   scale         softmax scale (usually 1/sqrt(D))
  *   out           [batch, Hq, D] bf16 (device)
  *   workspace     device scratch of at least
- *                 pka_decode_workspace_bytes(geom, batch, max_seq_len) bytes
- *                 (may be NULL when that size is 0). Contents on entry are ignored.
- * Supported: D == 128, Hq/Hkv <= 16. batch == 0 is a no-op.
+ *                 pka_decode_workspace_bytes(geom, batch, max_seq_len) bytes (may be
+ *                 NULL when that size is 0). Contents on entry are ignored. Calls
+ *                 that run concurrently must not share a workspace.
+ * Supported: D == 128, Hq/Hkv <= 16, batch <= 4096 (else PKA_E_UNSUPPORTED).
+ * batch == 0 is a no-op.
  */
 int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* page_table,

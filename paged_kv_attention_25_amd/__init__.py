@@ -155,7 +155,8 @@ def _alloc_like(q, nbytes):
 
 def paged_attn_decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, page_size, scale,
                       out=None, workspace=None):
-    """pka_paged_attn_decode. q [B, Hq, D]; returns out [B, Hq, D] (same dtype as q)."""
+    """pka_paged_attn_decode. q [B, Hq, D]; returns out [B, Hq, D] (same dtype as q).
+    Without a workspace, one of pka_decode_workspace_bytes is allocated for the call."""
     import torch
     g = _pool_geom(q.shape[1], k_pool, page_size)
     batch = int(q.shape[0])

@@ -1,31 +1,51 @@
-// Paged GQA decode for gfx950: split over the key axis, then a merge pass.
+// Paged GQA decode for gfx950: persistent wavefronts over a dense list of key
+// chunks, then a merge pass for requests split over several chunks.
 //
 // Batched decode reads every request's keys from the paged pool through its page
 // table ("miniSGLang intro blog", section 1.3; "Mini-SGLang deployment guide",
 // sections 6.2 and 6.3, where decode has its own kernel).
 //
-// Work unit = (request b, kv head g, split s): one wavefront attends the G q heads
-// of kv head g to keys [s*chunk, min((s+1)*chunk, L_b)). The G q heads are the
-// columns of 16x16x32 bf16 MFMA tiles (padded to 16 with zero queries), 32 keys at
-// a time:
-//   S^T[key][head] = K . Q^T   (A = K rows, B = Q; 4 MFMAs per 16 keys over D=128)
-//   O^T[d][head] += V^T . P^T  (A = V^T, B = P^T; 8 MFMAs over 32 keys)
-// Index choices that make every operand a plain load:
-//  * QK reduction order: lane l feeds d = 32*(l/16) + 8c + j to MFMA c, so each
-//    lane reads 64 contiguous bytes of one key row (K) and of one query row (Q).
-//  * PV key order: the 32 keys of a step are fed so that lane group l/16 takes keys
-//    {4*(l/16)+j, 16+4*(l/16)+j}, exactly the keys whose scores it holds after QK,
-//    so P^T needs no data movement.
-//  * Output rows: row m of O^T tile t is d = 8m + t, so lane l loads 16 contiguous
-//    bytes V[key][8*(l%16) .. +8] per key (16 lanes read one 256-byte row: fully
-//    coalesced) and an in-register 8x8 transpose of bf16 pairs forms the operands.
-// Softmax is online in the log2 domain (scale*log2(e) folded into one multiply);
-// the running sum stays a per-lane partial until the end.
+// Work decomposition. A request of L_b keys is cut into S_b = ceil(L_b / chunk)
+// chunks; a work unit is (request b, kv head g, chunk s). Each workgroup first
+// builds, in LDS, the prefix sums of S_b over the batch (and a copy of seq_lens),
+// so units are numbered densely (no empty units) with the kv head fastest. Every
+// wavefront is an independent worker over a fixed share of the units (wavefront w
+// of W takes units w, w + W, w + 2W, ...): it streams a unit's 64-key blocks,
+// writes the unit's output (or partial output) and moves on. Nothing synchronises
+// the wavefronts, and moving to the next unit reads only LDS, so a unit boundary
+// costs no memory round trip.
 //
-// A request whose keys fit in one chunk is written to `out` directly (bf16).
-// Otherwise each split writes its normalised partial output (f32) and its
-// log2-sum-exp to the workspace and the merge kernel combines them:
+// Streaming. A wavefront holds one 64-key block (32 KB of K/V at 256-byte head
+// rows) in registers. After computing a block it issues the loads of the next block
+// - possibly in the next unit - then moves its cursor (LDS only) and issues the
+// page-table entries of the block after that (one entry per lane covers 64 keys).
+// Page-table entries are consumed only after the next compute, so waiting for them
+// never drains K/V loads issued after them (vmcnt counts vector memory operations
+// in issue order).
+//
+// Per block, the G q heads of kv head g are the columns of 16x16x32 bf16 MFMA
+// tiles (padded to 16 with zero queries):
+//   S^T[key][head] = K . Q^T   (A = K rows, B = Q; 16 MFMAs per 64 keys)
+//   O^T[d][head] += V^T . P^T  (A = V^T, B = P^T; 16 MFMAs per 64 keys)
+// Index choices that make every operand a plain load:
+//  * QK: MFMA c reduces over d = 32c .. 32c+31; lane group l/16 feeds d = 32c +
+//    8*(l/16) .. +8, so one load instruction reads a whole 64-byte sector of each of
+//    16 key rows.
+//  * PV key order: in each 32-key half, lane group l/16 feeds keys {4*(l/16)+j,
+//    16+4*(l/16)+j}, exactly the keys whose scores it holds after QK, so P^T needs
+//    no data movement.
+//  * Output rows: row m of O^T tile t is d = 8m + t, so lane l loads 16 contiguous
+//    bytes V[key][8*(l%16) .. +8] per key (16 lanes read one 256-byte row) and an
+//    in-register 8x8 transpose of bf16 pairs forms the operands.
+// Softmax is online in the log2 domain (scale*log2(e) folded into one multiply).
+//
+// A request that fits in one chunk is written to `out` directly (bf16). Otherwise
+// each chunk writes its normalised partial output (f32) and log2-sum-exp to the
+// workspace, and the merge kernel combines them:
 //   LSE = log2 sum_s 2^lse_s,  out = sum_s 2^(lse_s - LSE) * o_s.
+//
+// Workspace layout (only when some request can span several chunks): partial
+// outputs [B, Hq, S, D] f32, then their log2-sum-exps [B, Hq, S] f32.
 #include "pka_device.h"
 #include "pka_kernels.h"
 
@@ -33,7 +53,11 @@ namespace pka {
 
 namespace {
 
-constexpr int kKeysPerStep = 32;
+constexpr int kBlock = 64;        // keys per wavefront block
+constexpr int kWaves = 4;         // wavefronts per workgroup (sharing the LDS tables)
+constexpr int kMaxBatchLds = 4096;
+constexpr int kMaxGroup = 16;
+constexpr int kPlanWaves = 2048;  // resident wavefronts assumed by the chunk plan
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct DecodeKernelArgs {
@@ -43,10 +67,11 @@ struct DecodeKernelArgs {
   const int32_t* __restrict__ page_table;
   const int32_t* __restrict__ seq_lens;
   uint16_t* __restrict__ out;
-  float* __restrict__ part_o;    // [B, Hq, S, D]
-  float* __restrict__ part_lse;  // [B, Hq, S]
+  float* __restrict__ part_o;      // [B, Hq, S, D]
+  float* __restrict__ part_lse;    // [B, Hq, S]
   PageGeom pg;
   int32_t pt_stride;
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
@@ -55,173 +80,362 @@ struct DecodeKernelArgs {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeKernelArgs p) {
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int n = lane & 15;   // MFMA row/column index of this lane
-  const int grp = lane >> 4; // MFMA reduction group of this lane
+struct Lds {
+  int32_t prefix[kMaxBatchLds + 1];  // prefix sums of chunks per request
+  int32_t seq_len[kMaxBatchLds];     // copy of seq_lens
+  int32_t wave_tot[kWaves];
+};
 
-  const int L = p.seq_lens[b];
-  const int start = s * p.chunk;
-  if (start >= L) return;
-  const int end = min(start + p.chunk, L);
-  const bool single = L <= p.chunk;
+// Register-resident q, K and V of one 64-key block.
+struct Block {
+  u32x4 q[4];      // Q^T operand: q head n, d = 32c + 8*grp .. +8 (zero for n >= G)
+  u32x4 k[4][4];   // [16-key group s][c]: key 16s + n, d = 32c + 8*grp .. +8
+  u32x4 v[2][8];   // [32-key half h][j]: key 32h + {4grp+j | 16+4grp+(j-4)}, d = 8n .. +8
+};
 
+struct Unit {
+  int32_t id;  // -1 = none
+  int32_t b, g, s, start, end, L;
+};
+
+// One block of a wavefront's stream.
+struct Desc {
+  int32_t valid;
+  int32_t b, g, s;
+  int32_t k0, end, L;
+  int32_t last;  // last block of its unit
+};
+
+struct SoftmaxState {
+  float m;     // running max of this lane's column (log2 domain)
+  float lsum;  // this lane's share of the running sum
+  f32x4 o[8];  // O^T tiles: lane holds d = 32*grp + 8v + t in o[t][v]
+};
+
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ Unit unit_info(int32_t u, int32_t total, const DecodeKernelArgs& p,
+                                          const Lds& lds) {
+  Unit un;
+  un.id = -1;
+  un.b = un.g = un.s = un.start = un.end = un.L = 0;
+  if (u >= total) return un;
+  const int32_t pair = u / p.num_kv_heads;
+  un.id = u;
+  un.g = u - pair * p.num_kv_heads;
+  // largest b with prefix[b] <= pair (requests with no chunks have empty ranges)
+  int32_t lo = 0, hi = p.batch;  // prefix[lo] <= pair < prefix[hi]
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (uniform(lds.prefix[mid]) <= pair) lo = mid; else hi = mid;
+  }
+  un.b = lo;
+  un.s = pair - uniform(lds.prefix[lo]);
+  un.L = uniform(lds.seq_len[lo]);
+  un.start = un.s * p.chunk;
+  un.end = min(un.start + p.chunk, un.L);
+  return un;
+}
+
+// The wavefront's cursor: the unit it is in and the next block's start. Units
+// follow with a stride of `stride` (the number of wavefronts).
+struct Cursor {
+  Unit un;
+  int32_t k0;
+  int32_t stride;
+};
+
+__device__ __forceinline__ Desc cursor_next(Cursor& c, int32_t total, const DecodeKernelArgs& p,
+                                            const Lds& lds) {
+  Desc d;
+  d.valid = c.un.id >= 0;
+  d.b = c.un.b;
+  d.g = c.un.g;
+  d.s = c.un.s;
+  d.k0 = c.k0;
+  d.end = c.un.end;
+  d.L = c.un.L;
+  d.last = c.k0 + kBlock >= c.un.end;
+  if (!d.valid) return d;
+  c.k0 += kBlock;
+  if (c.k0 >= c.un.end) {
+    c.un = unit_info(c.un.id + c.stride, total, p, lds);
+    c.k0 = c.un.start;
+  }
+  return d;
+}
+
+// Page-table entry of key (block start + lane), loaded but not yet used: the slot
+// arithmetic runs in resolve(), after the current block's compute.
+struct RawSlot {
+  int32_t page;  // loaded page id
+  int32_t off;   // offset in the page; -1 when the key's table index is past the row
+};
+
+__device__ __forceinline__ RawSlot lookup_raw(const Desc& d, int lane, const DecodeKernelArgs& p) {
+  RawSlot r;
+  r.page = 0;
+  r.off = -1;
+  if (!d.valid) return r;
+  // keys past the block's end are clamped to the last valid key (loaded, masked)
+  const int32_t key = min(d.k0 + lane, d.end - 1);
+  int32_t idx;
+  if (p.pg.page_shift >= 0) {
+    idx = key >> p.pg.page_shift;
+    r.off = key & (p.pg.page_size - 1);
+  } else {
+    idx = key / p.pg.page_size;
+    r.off = key - idx * p.pg.page_size;
+  }
+  if (idx < 0 || idx >= p.pg.table_width) {
+    r.off = -1;
+  } else {
+    r.page = p.page_table[(int64_t)d.b * p.pt_stride + idx];
+  }
+  return r;
+}
+
+// Keep the compiler from using (and so waiting for) `x` before this point.
+template <typename T>
+__device__ __forceinline__ void hold(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+__device__ __forceinline__ int32_t resolve(RawSlot r, const DecodeKernelArgs& p) {
+  hold(r.page);
+  const bool ok = r.off >= 0 && r.page >= 0 && (int64_t)r.page < p.pg.num_pages;
+  return ok ? r.page * p.pg.page_size + r.off : -1;
+}
+
+// Issue the loads of one block. `slot` is this lane's slot of key (block start +
+// lane). A key whose page id is outside the pool (slot -1) reads slot 0 instead: the
+// access stays in bounds and that request's result is unspecified.
+__device__ __forceinline__ void load_block(Block& blk, const Desc& d, int32_t slot, int n, int grp,
+                                           const DecodeKernelArgs& p) {
   const int64_t row_elems = (int64_t)p.num_kv_heads * kHeadDim;
-  const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_stride;
-  const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim;
-  const uint16_t* vbase = p.v_pool + (int64_t)g * kHeadDim;
-
-  // Q^T operand: column n is q head g*G + n (zero for n >= G).
-  const int h = g * p.group + n;
-  u32x4 qv[4];
+  const uint16_t* kbase = p.k_pool + (int64_t)d.g * kHeadDim + 8 * grp;
+  const uint16_t* vbase = p.v_pool + (int64_t)d.g * kHeadDim + 8 * n;
   if (n < p.group) {
-    const u32x4* qrow =
-        (const u32x4*)(p.q + ((int64_t)b * p.num_q_heads + h) * kHeadDim + 32 * grp);
+    const uint16_t* qrow =
+        p.q + ((int64_t)d.b * p.num_q_heads + d.g * p.group + n) * kHeadDim + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qv[c] = qrow[c];
+    for (int c = 0; c < 4; ++c) blk.q[c] = *(const u32x4*)(qrow + 32 * c);
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qv[c] = u32x4{0, 0, 0, 0};
+    for (int c = 0; c < 4; ++c) blk.q[c] = u32x4{0, 0, 0, 0};
   }
-
-  float m = kNegInf;  // running max of this column (log2 domain)
-  float lsum = 0.f;   // this lane's share of the running sum
-  f32x4 o[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = start; kb < end; kb += 2 * kKeysPerStep) {
-    // One page-table lookup per lane covers 64 keys; keys past `end` are clamped to
-    // the last valid key (loaded but masked out of the softmax).
-    const int32_t my_slot = slot_of(pt_row, min(kb + lane, end - 1), p.pg);
+  for (int s = 0; s < 4; ++s) {
+    const int32_t sk = max(__shfl(slot, 16 * s + n), 0);
+    const uint16_t* kp = kbase + (int64_t)sk * row_elems;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k0 = kb + half * kKeysPerStep;
-      if (k0 >= end) break;
-      const int base_lane = half * kKeysPerStep;
-      // K rows of keys k0+n and k0+16+n: 64 bytes each, d from 32*grp.
-      const int32_t sk0 = __shfl(my_slot, base_lane + n);
-      const int32_t sk1 = __shfl(my_slot, base_lane + 16 + n);
-      u32x4 k0r[4], k1r[4];
-      if (sk0 >= 0) {
-        const u32x4* src = (const u32x4*)(kbase + (int64_t)sk0 * row_elems + 32 * grp);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) k0r[c] = src[c];
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) k0r[c] = u32x4{0, 0, 0, 0};
-      }
-      if (sk1 >= 0) {
-        const u32x4* src = (const u32x4*)(kbase + (int64_t)sk1 * row_elems + 32 * grp);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) k1r[c] = src[c];
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) k1r[c] = u32x4{0, 0, 0, 0};
-      }
-      // V rows of this lane's 8 PV keys: 16 bytes each, d = 8n .. 8n+7.
-      u32x4 vr[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kl = (j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4));
-        const int32_t sv = __shfl(my_slot, base_lane + kl);
-        if (sv >= 0) {
-          vr[j] = *(const u32x4*)(vbase + (int64_t)sv * row_elems + 8 * n);
-        } else {
-          vr[j] = u32x4{0, 0, 0, 0};
-        }
-      }
-
-      // Scores: lane holds column n (q head), keys k0 + 4*grp + v and k0 + 16 + 4*grp + v.
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s0 = mfma_16x16x32(k0r[c], qv[c], s0);
-        s1 = mfma_16x16x32(k1r[c], qv[c], s1);
-      }
-      float sc[8];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key0 = k0 + 4 * grp + v;
-        sc[v] = (key0 < end) ? s0[v] * p.scale_log2 : kNegInf;
-        sc[4 + v] = (key0 + 16 < end) ? s1[v] * p.scale_log2 : kNegInf;
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);  // finite: key k0 is always valid
-      const float alpha = fast_exp2(m - m_new);
-      float pr[8];
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = fast_exp2(sc[i] - m_new);
-        ps += pr[i];
-      }
-      lsum = lsum * alpha + ps;
-      m = m_new;
-      u32x4 pb;
-      pb[0] = pack_bf16x2(pr[0], pr[1]);
-      pb[1] = pack_bf16x2(pr[2], pr[3]);
-      pb[2] = pack_bf16x2(pr[4], pr[5]);
-      pb[3] = pack_bf16x2(pr[6], pr[7]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int w = t >> 1;
-        u32x4 a;
-        if ((t & 1) == 0) {
-          a[0] = lo_halves(vr[0][w], vr[1][w]);
-          a[1] = lo_halves(vr[2][w], vr[3][w]);
-          a[2] = lo_halves(vr[4][w], vr[5][w]);
-          a[3] = lo_halves(vr[6][w], vr[7][w]);
-        } else {
-          a[0] = hi_halves(vr[0][w], vr[1][w]);
-          a[1] = hi_halves(vr[2][w], vr[3][w]);
-          a[2] = hi_halves(vr[4][w], vr[5][w]);
-          a[3] = hi_halves(vr[6][w], vr[7][w]);
-        }
-        o[t] = o[t] * alpha;
-        o[t] = mfma_16x16x32(a, pb, o[t]);
-      }
-    }
+    for (int c = 0; c < 4; ++c) blk.k[s][c] = *(const u32x4*)(kp + 32 * c);
   }
-
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (n >= p.group) return;
-  const float inv = 1.f / ltot;
-  // Lane holds d = 32*grp + 8v + t for t = 0..7 in o[t][v].
-  if (single) {
-    uint16_t* dst = p.out + ((int64_t)b * p.num_q_heads + h) * kHeadDim + 32 * grp;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      u32x4 w;
-      w[0] = pack_bf16x2(o[0][v] * inv, o[1][v] * inv);
-      w[1] = pack_bf16x2(o[2][v] * inv, o[3][v] * inv);
-      w[2] = pack_bf16x2(o[4][v] * inv, o[5][v] * inv);
-      w[3] = pack_bf16x2(o[6][v] * inv, o[7][v] * inv);
-      *(u32x4*)(dst + 8 * v) = w;
-    }
-  } else {
-    const int64_t unit = ((int64_t)b * p.num_q_heads + h) * p.num_splits + s;
-    float* dst = p.part_o + unit * kHeadDim + 32 * grp;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      f32x4 lo = {o[0][v] * inv, o[1][v] * inv, o[2][v] * inv, o[3][v] * inv};
-      f32x4 hi = {o[4][v] * inv, o[5][v] * inv, o[6][v] * inv, o[7][v] * inv};
-      *(f32x4*)(dst + 8 * v) = lo;
-      *(f32x4*)(dst + 8 * v + 4) = hi;
+    for (int j = 0; j < 8; ++j) {
+      const int kl = 32 * h + ((j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4)));
+      const int32_t sv = max(__shfl(slot, kl), 0);
+      blk.v[h][j] = *(const u32x4*)(vbase + (int64_t)sv * row_elems);
     }
-    if (grp == 0) p.part_lse[unit] = m + __builtin_log2f(ltot);
   }
 }
 
-// One wavefront per (request, q head): lane l combines d = 2l, 2l+1 over the splits.
+__device__ __forceinline__ void reset_state(SoftmaxState& st) {
+  st.m = kNegInf;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ void compute_block(const Block& blk, const Desc& d, int grp,
+                                              float scale_log2, SoftmaxState& st) {
+  // Scores: lane holds column n (q head), keys k0 + 16s + 4*grp + v in sacc[s][v].
+  f32x4 sacc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc[s] = mfma_16x16x32(blk.k[s][c], blk.q[c], sacc[s]);
+  }
+  float sc[16];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int key = d.k0 + 16 * s + 4 * grp + v;
+      sc[4 * s + v] = (key < d.end) ? sacc[s][v] * scale_log2 : kNegInf;
+    }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);  // finite: key k0 is always valid
+  const float alpha = fast_exp2(st.m - m_new);
+  float pr[16];
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    pr[i] = fast_exp2(sc[i] - m_new);
+    ps += pr[i];
+  }
+  st.lsum = st.lsum * alpha + ps;
+  st.m = m_new;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = st.o[t] * alpha;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // P^T operand of half h: slots j<4 -> group 2h, j>=4 -> group 2h+1
+    u32x4 pb;
+    pb[0] = pack_bf16x2(pr[8 * h + 0], pr[8 * h + 1]);
+    pb[1] = pack_bf16x2(pr[8 * h + 2], pr[8 * h + 3]);
+    pb[2] = pack_bf16x2(pr[8 * h + 4], pr[8 * h + 5]);
+    pb[3] = pack_bf16x2(pr[8 * h + 6], pr[8 * h + 7]);
+    const u32x4* vv = blk.v[h];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int w = t >> 1;
+      u32x4 a;
+      if ((t & 1) == 0) {
+        a[0] = lo_halves(vv[0][w], vv[1][w]);
+        a[1] = lo_halves(vv[2][w], vv[3][w]);
+        a[2] = lo_halves(vv[4][w], vv[5][w]);
+        a[3] = lo_halves(vv[6][w], vv[7][w]);
+      } else {
+        a[0] = hi_halves(vv[0][w], vv[1][w]);
+        a[1] = hi_halves(vv[2][w], vv[3][w]);
+        a[2] = hi_halves(vv[4][w], vv[5][w]);
+        a[3] = hi_halves(vv[6][w], vv[7][w]);
+      }
+      st.o[t] = mfma_16x16x32(a, pb, st.o[t]);
+    }
+  }
+}
+
+// Write one unit's result: bf16 output when the request has a single chunk, else the
+// normalised partial output and its log2-sum-exp.
+__device__ __forceinline__ void finish_unit(const Desc& d, SoftmaxState& st, int n, int grp,
+                                            const DecodeKernelArgs& p) {
+  float ltot = st.lsum + __shfl_xor(st.lsum, 16);
+  ltot += __shfl_xor(ltot, 32);
+  const float inv = 1.f / ltot;
+  if (n < p.group) {
+    const int h = d.g * p.group + n;
+    if (d.L <= p.chunk) {
+      uint16_t* dst = p.out + ((int64_t)d.b * p.num_q_heads + h) * kHeadDim + 32 * grp;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        u32x4 w;
+        w[0] = pack_bf16x2(st.o[0][v] * inv, st.o[1][v] * inv);
+        w[1] = pack_bf16x2(st.o[2][v] * inv, st.o[3][v] * inv);
+        w[2] = pack_bf16x2(st.o[4][v] * inv, st.o[5][v] * inv);
+        w[3] = pack_bf16x2(st.o[6][v] * inv, st.o[7][v] * inv);
+        *(u32x4*)(dst + 8 * v) = w;
+      }
+    } else {
+      const int64_t unit = ((int64_t)d.b * p.num_q_heads + h) * p.num_splits + d.s;
+      float* dst = p.part_o + unit * kHeadDim + 32 * grp;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        *(f32x4*)(dst + 8 * v) =
+            f32x4{st.o[0][v] * inv, st.o[1][v] * inv, st.o[2][v] * inv, st.o[3][v] * inv};
+        *(f32x4*)(dst + 8 * v + 4) =
+            f32x4{st.o[4][v] * inv, st.o[5][v] * inv, st.o[6][v] * inv, st.o[7][v] * inv};
+      }
+      if (grp == 0) p.part_lse[unit] = st.m + __builtin_log2f(ltot);
+    }
+  }
+  reset_state(st);
+}
+
+// Two wavefronts per SIMD (256 registers each).
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_split_kernel(DecodeKernelArgs p) {
+  __shared__ Lds lds;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;   // MFMA row/column index of this lane
+  const int grp = lane >> 4; // MFMA reduction group of this lane
+
+  // Prefix sums of chunks per request (blocked scan: each thread owns a run of
+  // consecutive requests) and a copy of seq_lens.
+  const int per = (p.batch + kWaves * 64 - 1) / (kWaves * 64);
+  const int b0 = tid * per;
+  int32_t run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.batch) {
+      const int32_t L = p.seq_lens[b];
+      lds.seq_len[b] = L;
+      run += L > 0 ? min((L + p.chunk - 1) / p.chunk, p.num_splits) : 0;
+    }
+  }
+  int32_t incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) lds.wave_tot[wave] = incl;
+  __syncthreads();
+  int32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += lds.wave_tot[w];
+  int32_t excl = base + incl - run;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < p.batch) {
+      lds.prefix[b] = excl;
+      const int32_t L = lds.seq_len[b];
+      excl += L > 0 ? min((L + p.chunk - 1) / p.chunk, p.num_splits) : 0;
+    }
+  }
+  if (tid == kWaves * 64 - 1) lds.prefix[p.batch] = excl;
+  __syncthreads();
+  const int32_t total = uniform(lds.prefix[p.batch]) * p.num_kv_heads;
+
+  SoftmaxState st;
+  reset_state(st);
+  Cursor cur;
+  cur.stride = (int32_t)gridDim.x * kWaves;
+  cur.un = unit_info((int32_t)blockIdx.x * kWaves + wave, total, p, lds);
+  cur.k0 = cur.un.start;
+
+  Block blk;
+  Desc d = cursor_next(cur, total, p, lds);
+  if (d.valid) load_block(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
+  Desc dn = cursor_next(cur, total, p, lds);
+  RawSlot raw_n = lookup_raw(dn, lane, p);
+
+  while (d.valid) {
+    compute_block(blk, d, grp, p.scale_log2, st);
+    // The next block's loads go out first; the cursor (LDS only), the page-table
+    // entries of the block after and this unit's stores follow.
+    const int32_t slot_n = resolve(raw_n, p);
+    if (dn.valid) load_block(blk, dn, slot_n, n, grp, p);
+    const Desc dnn = cursor_next(cur, total, p, lds);
+    raw_n = lookup_raw(dnn, lane, p);
+    if (d.last) finish_unit(d, st, n, grp, p);
+    d = dn;
+    dn = dnn;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wavefront per (request, q head): the split weights are computed once (lane s
+// holds split s), then lane l combines d = 2l, 2l+1 over the splits, four at a time.
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ seq_lens,
@@ -232,38 +446,81 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int L = seq_lens[b];
+  if (L <= chunk) return;  // written directly by the split kernel
   // Keys past num_splits * chunk (a length above the planned maximum) were not
   // attended, so only the planned splits exist in the workspace.
   const int nsplit = min((L + chunk - 1) / chunk, num_splits);
-  if (L <= chunk) return;  // written directly by the split kernel
   const int64_t unit0 = ((int64_t)b * num_q_heads + h) * num_splits;
   float mx = kNegInf;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[unit0 + s]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    mx = fmaxf(mx, s0 + lane < nsplit ? part_lse[unit0 + s0 + lane] : kNegInf);
+  mx = wave_max(mx);
   float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = fast_exp2(part_lse[unit0 + s] - mx);
-    const float2 v = *(const float2*)(part_o + (unit0 + s) * kHeadDim + 2 * lane);
-    wsum += w;
-    acc0 += w * v.x;
-    acc1 += w * v.y;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const float w_l = s0 + lane < nsplit ? fast_exp2(part_lse[unit0 + s0 + lane] - mx) : 0.f;
+    wsum += w_l;
+    const int cnt = min(64, nsplit - s0);
+    const float* src = part_o + (unit0 + s0) * kHeadDim + 2 * lane;
+    int s = 0;
+    for (; s + 4 <= cnt; s += 4) {
+      float2 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *(const float2*)(src + (int64_t)(s + i) * kHeadDim);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w = __shfl(w_l, s + i);
+        acc0 += w * v[i].x;
+        acc1 += w * v[i].y;
+      }
+    }
+    for (; s < cnt; ++s) {
+      const float2 v = *(const float2*)(src + (int64_t)s * kHeadDim);
+      const float w = __shfl(w_l, s);
+      acc0 += w * v.x;
+      acc1 += w * v.y;
+    }
   }
-  const float inv = 1.f / wsum;
+  const float inv = 1.f / wave_sum(wsum);
   uint32_t* dst = (uint32_t*)(out + ((int64_t)b * num_q_heads + h) * kHeadDim);
   dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
 }
 
+int device_workgroups() {
+  // Resident workgroups: 2 per CU (8 wavefronts of 256 registers each).
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanWaves / kWaves;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = kPlanWaves / (2 * kWaves);
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
-DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
-  // Aim for about 8192 work units (32 per CU on 256 CUs) counted against the upper
-  // bound batch * max_seq_len, with chunks a multiple of 64 keys in [64, 4096].
+bool decode_supported(int32_t batch, int32_t group) {
+  return batch <= kMaxBatchLds && group <= kMaxGroup;
+}
+
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len) {
+  // Largest power-of-two chunk in [max(128, 16*G), 4096] whose upper-bound unit count
+  // (every request at max_seq_len) reaches 8 units per resident wavefront, so the
+  // round-robin assignment balances well; the floor keeps a chunk's partial output
+  // (G*D floats, written and read back once) near 3% of its K/V bytes.
   DecodePlan plan;
-  const int64_t work = (int64_t)batch * num_kv_heads * (int64_t)(max_seq_len > 0 ? max_seq_len : 1);
-  int64_t chunk = 64;
-  while (chunk < 4096 && work / chunk > 8192) chunk *= 2;
+  const int64_t pairs = (int64_t)batch * num_kv_heads;
+  const int64_t msl = max_seq_len > 0 ? max_seq_len : 1;
+  int64_t floor_chunk = 16 * (int64_t)group;
+  if (floor_chunk < 2 * kBlock) floor_chunk = 2 * kBlock;
+  int64_t chunk = 4096;
+  while (chunk > floor_chunk && pairs * ((msl + chunk - 1) / chunk) < 8 * kPlanWaves) chunk >>= 1;
+  if (chunk < floor_chunk) chunk = floor_chunk;
   plan.chunk = (int32_t)chunk;
-  plan.num_splits = (int32_t)((max_seq_len + chunk - 1) / chunk);
-  if (plan.num_splits < 1) plan.num_splits = 1;
+  plan.num_splits = (int32_t)((msl + chunk - 1) / chunk);
   return plan;
 }
 
@@ -290,14 +547,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   k.pg.num_pages = a.num_pages;
   k.pg.table_width = a.pt_stride;
   k.pt_stride = a.pt_stride;
+  k.batch = a.batch;
   k.num_q_heads = a.num_q_heads;
   k.num_kv_heads = a.num_kv_heads;
   k.group = a.num_q_heads / a.num_kv_heads;
   k.chunk = plan.chunk;
   k.num_splits = plan.num_splits;
   k.scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(plan.num_splits, a.num_kv_heads, a.batch),
-                     dim3(64), 0, stream, k);
+  const int64_t max_units = (int64_t)a.batch * a.num_kv_heads * plan.num_splits;
+  int64_t grid = device_workgroups();
+  if (grid * kWaves > max_units) grid = (max_units + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.num_splits <= 1) return err;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(a.num_q_heads, a.batch), dim3(64), 0, stream,

@@ -27,7 +27,9 @@ struct DecodePlan {
   int32_t chunk;
   int32_t num_splits;  // ceil(max_seq_len / chunk)
 };
-DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len);
+// Whether the decode kernel supports this batch size and group size (q heads per kv head).
+bool decode_supported(int32_t batch, int32_t group);
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, const DecodePlan& plan);
 
 struct DecodeArgs {

@@ -72,7 +72,7 @@ def prefill(L, g, batch=2, tokens=10, max_ext=6, max_seq=20, stride=20, q=FAKE):
 
 def test_workspace_sizes(L):
     g = geom()
-    # one 64-key chunk covers everything: no split, no workspace
+    # one chunk covers everything: no split, no workspace
     assert L.pka_decode_workspace_bytes(ctypes.byref(g), 1, 64) == 0
     # long sequences split: partial o (D floats) + lse per (request, q head, split)
     n = L.pka_decode_workspace_bytes(ctypes.byref(g), 32, 32768)
