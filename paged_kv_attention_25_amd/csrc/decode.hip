@@ -195,12 +195,6 @@ __device__ __forceinline__ RawSlot lookup_raw(const Desc& d, int lane, const Dec
   return r;
 }
 
-// Keep the compiler from using (and so waiting for) `x` before this point.
-template <typename T>
-__device__ __forceinline__ void hold(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
 __device__ __forceinline__ int32_t resolve(RawSlot r, const DecodeKernelArgs& p) {
   hold(r.page);
   const bool ok = r.off >= 0 && r.page >= 0 && (int64_t)r.page < p.pg.num_pages;

@@ -47,6 +47,13 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t x, uint32_t y) {
   return (x >> 16) | (y & 0xffff0000u);
 }
 
+// Keep the compiler from using (and so waiting for) a loaded value `x` before this
+// point: the load's latency overlaps with whatever comes before.
+template <typename T>
+__device__ __forceinline__ void hold(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Page-table geometry: token j of a request lives in slot table[j / P] * P + j % P.

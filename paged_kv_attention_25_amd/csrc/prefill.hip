@@ -9,8 +9,9 @@
 // Tiling. A workgroup of 4 wavefronts owns 128 query rows of one (request, kv head).
 // Rows are (token, head-in-group) pairs, row r = i*G + hh, so the G q heads that
 // share a kv head share every K/V tile. Each wavefront owns 32 rows. Keys are
-// processed in tiles of 64: the tile's K and V rows are gathered through the page
-// table into LDS (row pitch 272 bytes to spread LDS banks), with the next tile's
+// processed in tiles of 64: the tile's K rows are gathered through the page table
+// into LDS row-major (272-byte pitch), its V rows transposed into LDS (V^T, one row
+// per d, 144-byte pitch, 16-byte chunks XOR-swizzled by row), with the next tile's
 // global loads in flight while the current tile is computed.
 //
 // Per wavefront and tile, with 32x32x16 bf16 MFMAs:
@@ -20,11 +21,14 @@
 //  * QK reduction order: lane l feeds d = 16c + 8*(l/32) + j to MFMA c, a 16-byte
 //    LDS read of K and a 16-byte global read of Q.
 //  * PV key order: MFMA u takes keys 16u + 8*(j/4) + 4*(l/32) + (j%4), which are
-//    exactly the scores lane l already holds, so P^T needs no data movement.
-//  * Output rows: row m of O^T tile t is d = 4m + t, so a lane reads 8 bytes
-//    V[key][4*(l%32) .. +4] per key and transposes 4x8 bf16 in registers.
-// Online softmax in the log2 domain, causal mask only on tiles that cross the
-// diagonal, tiles past the last row's position skipped.
+//    exactly the scores lane l already holds, so P^T needs no data movement. V^T
+//    stores key k of a 16-key group at position k with bits 2 and 3 swapped, which
+//    makes those 8 keys contiguous: each V^T operand is one 16-byte LDS read.
+// Softmax runs in the log2 domain with the scale folded into one FMA per score. The
+// running max is only raised (and the output rescaled) when it grows by more than
+// 2^8, so most tiles skip the rescale; probabilities stay below 2^8 in between.
+// Causal masking only on tiles that cross a wavefront's diagonal; tiles past the
+// last row's position are skipped.
 #include "pka_device.h"
 #include "pka_kernels.h"
 
@@ -36,7 +40,9 @@ constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 128
 constexpr int kKeysPerTile = 64;
-constexpr int kLdsPitch = kHeadDim + 8;  // elements; 272 bytes per row
+constexpr int kLdsPitch = kHeadDim + 8;     // K rows: elements; 272 bytes per row
+constexpr int kVtPitch = kKeysPerTile + 8;  // V^T rows: elements; 144 bytes per row
+constexpr float kRescaleLog2 = 8.f;         // raise the running max past 2^8 growth
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct PrefillKernelArgs {
@@ -59,7 +65,16 @@ struct PrefillKernelArgs {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
+// Position of key k (0..63) of a tile in the V^T rows: bits 2 and 3 swapped.
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+// V^T row d keeps its eight 16-byte chunks XOR-swizzled by (d / 16) % 8, so that both
+// the transposing 8-byte writes and the 16-byte operand reads spread over all banks.
+
+// Two workgroups (8 wavefronts) per CU.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_kernel(PrefillKernelArgs p) {
   // Block id -> (q tile, request, kv head); the highest q tiles (the most keys)
   // are dispatched first, and with the kv head fastest all tiles of one
   // (request, kv head) land on the same XCD when the head count divides 8.
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
   const int wave_lim_hi = prefix + (wave_live ? wrow_last / G : 0);
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeysPerTile * kLdsPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kKeysPerTile * kLdsPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVtPitch];
 
   // Q^T operand: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
   u32x4 qv[8];
@@ -116,35 +131,70 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
     for (int c = 0; c < 8; ++c) qv[c] = u32x4{0, 0, 0, 0};
   }
 
-  // Global -> LDS staging: thread covers 16-byte chunk (tid % 16) of keys tid/16 + 16i.
+  // Global -> LDS staging: thread covers 16-byte chunk m = tid % 16 (d = 8m .. 8m+7)
+  // of the four keys 4a .. 4a+3, a = tid / 16.
   const int64_t row_elems = (int64_t)p.num_kv_heads * kHeadDim;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_stride;
-  const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim + 8 * (tid & 15);
-  const uint16_t* vbase = p.v_pool + (int64_t)g * kHeadDim + 8 * (tid & 15);
-  const int ld_key = tid >> 4;
-  u32x4 kst[4], vst[4];
-  auto load_tile = [&](int kt) {
+  const int ld_m = tid & 15;
+  const int ld_a = tid >> 4;
+  const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim + 8 * ld_m;
+  const uint16_t* vbase = p.v_pool + (int64_t)g * kHeadDim + 8 * ld_m;
+  // Page-table entries of this thread's four keys of a tile are loaded one tile ahead
+  // of the K/V loads that use them, so no load waits on another in the loop. Every
+  // load is unconditional and in bounds: keys past the block's last key are clamped to
+  // it, a table index past the row to the row's last entry, and a page id outside the
+  // pool reads slot 0 (that request's result is then unspecified).
+  int32_t raw_page[4], raw_off[4];
+  auto lookup = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = min(kt + ld_key + 16 * i, key_end - 1);
-      const int32_t slot = slot_of(pt_row, key, p.pg);
-      if (slot >= 0) {
-        kst[i] = *(const u32x4*)(kbase + (int64_t)slot * row_elems);
-        vst[i] = *(const u32x4*)(vbase + (int64_t)slot * row_elems);
+      const int key = min(kt + 4 * ld_a + i, key_end - 1);
+      int idx;
+      if (p.pg.page_shift >= 0) {
+        idx = key >> p.pg.page_shift;
+        raw_off[i] = key & (p.pg.page_size - 1);
       } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
+        idx = key / p.pg.page_size;
+        raw_off[i] = key - idx * p.pg.page_size;
       }
+      raw_page[i] = pt_row[min(idx, p.pg.table_width - 1)];
     }
   };
+  u32x4 kst[4], vst[4];
+  auto load_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hold(raw_page[i]);
+      const int32_t page = raw_page[i];
+      const int32_t slot =
+          (uint32_t)page < (uint64_t)p.pg.num_pages ? page * p.pg.page_size + raw_off[i] : 0;
+      kst[i] = *(const u32x4*)(kbase + (int64_t)slot * row_elems);
+      vst[i] = *(const u32x4*)(vbase + (int64_t)slot * row_elems);
+    }
+  };
+  // K: row-major, key row at 272-byte pitch.
+  uint16_t* const k_st = k_lds + 4 * ld_a * kLdsPitch + 8 * ld_m;
+  // V^T: row d = 8m + j; the four keys land at positions vt_pos(4a) .. +3 of 16-byte
+  // chunk c = vt_pos(4a)/8, stored at chunk c ^ vt_swz(d) (8 bytes per row and key quad).
+  const int vq = vt_pos(4 * ld_a);
+  uint16_t* const vt_st = vt_lds + 8 * ld_m * kVtPitch + 8 * ((vq >> 3) ^ (ld_m >> 1)) + (vq & 7);
   auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int off = (ld_key + 16 * i) * kLdsPitch + 8 * (tid & 15);
-      *(u32x4*)(k_lds + off) = kst[i];
-      *(u32x4*)(v_lds + off) = vst[i];
+    for (int i = 0; i < 4; ++i) *(u32x4*)(k_st + i * kLdsPitch) = kst[i];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      u32x2 lo, hi;  // d = 8m + 2w and 8m + 2w + 1, keys 4a .. 4a+3
+      lo[0] = lo_halves(vst[0][w], vst[1][w]);
+      lo[1] = lo_halves(vst[2][w], vst[3][w]);
+      hi[0] = hi_halves(vst[0][w], vst[1][w]);
+      hi[1] = hi_halves(vst[2][w], vst[3][w]);
+      *(u32x2*)(vt_st + (2 * w) * kVtPitch) = lo;
+      *(u32x2*)(vt_st + (2 * w + 1) * kVtPitch) = hi;
     }
   };
+  // PV operand read base: V^T row col (+32t), chunk (2u + hgrp) ^ vt_swz(32t + col)
+  // = 2(u ^ t) + (hgrp ^ (col / 16)).
+  const uint16_t* const vt_rd = vt_lds + col * kVtPitch + 8 * (hgrp ^ (col >> 4));
 
   float m = kNegInf;
   float lsum = 0.f;
@@ -154,13 +204,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
 
-  load_tile(0);
+  lookup(0);
+  load_tile();
   store_tile();
+  lookup(kKeysPerTile);
   __syncthreads();
 
   for (int kt = 0; kt < key_end; kt += kKeysPerTile) {
     const bool has_next = kt + kKeysPerTile < key_end;
-    if (has_next) load_tile(kt + kKeysPerTile);
+    // Next tile's K/V and the page ids of the one after (past the end: clamped reloads).
+    load_tile();
+    lookup(kt + 2 * kKeysPerTile);
 
     if (wave_live && kt <= wave_lim_hi) {
       // S^T for two 32-key blocks.
@@ -176,26 +230,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
           sblk[kb2] = mfma_32x32x16(a, qv[c], sblk[kb2]);
         }
       }
-      // Scale, causal mask (only where the tile crosses the wave's diagonal), max.
-      const bool need_mask = kt + kKeysPerTile - 1 > wave_lim_lo;
+      // Causal mask only where the tile crosses this wavefront's diagonal: register i
+      // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
+      if (kt + kKeysPerTile - 1 > wave_lim_lo) {
+        const int dl = lim - kt - 4 * hgrp;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) sblk[kb2][i] = kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = sblk[kb2][i] * p.scale_log2;
-          if (need_mask) {
-            const int key = kt + kb2 * 32 + 8 * (i >> 2) + 4 * hgrp + (i & 3);
-            x = (key <= lim) ? x : kNegInf;
-          }
-          sblk[kb2][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sblk[kb2][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
+      // Raw-score max; the scale is applied inside the exponent. Rescale only when
+      // some row's max grew by more than 2^kRescaleLog2 (or has no value yet).
+      const bool grow = (mx - m) * p.scale_log2 > kRescaleLog2;
+      if (__any(grow)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
+        lsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = o[t] * alpha;
+        m = m_new;
+      }
+      const float neg_m = (m == kNegInf) ? 0.f : -m * p.scale_log2;
       float ps = 0.f;
       u32x4 pb[4];  // P^T operands for the 4 PV MFMAs (16 keys each)
 #pragma unroll
@@ -205,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
         float pr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pr[j] = fast_exp2(sblk[kb2][r0 + j] - m_use);
+          pr[j] = fast_exp2(fmaf(sblk[kb2][r0 + j], p.scale_log2, neg_m));
           ps += pr[j];
         }
         pb[u][0] = pack_bf16x2(pr[0], pr[1]);
@@ -213,35 +275,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
         pb[u][2] = pack_bf16x2(pr[4], pr[5]);
         pb[u][3] = pack_bf16x2(pr[6], pr[7]);
       }
-      lsum = lsum * alpha + ps;
-      m = m_new;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] = o[t] * alpha;
+      lsum += ps;
 
-      // O^T += V^T P^T. MFMA u covers keys 16u + 8*(j/4) + 4*hgrp + (j%4).
+      // O^T += V^T P^T: tile t covers d = 32t .. 32t+31; MFMA u takes the 16 keys at
+      // V^T positions 16u .. 16u+15, lane group hgrp the 8 at 16u + 8*hgrp.
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        u32x2 vk[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = 16 * u + 8 * (j >> 2) + 4 * hgrp + (j & 3);
-          vk[j] = *(const u32x2*)(v_lds + key * kLdsPitch + 4 * col);
-        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int w = t >> 1;
-          u32x4 a;
-          if ((t & 1) == 0) {
-            a[0] = lo_halves(vk[0][w], vk[1][w]);
-            a[1] = lo_halves(vk[2][w], vk[3][w]);
-            a[2] = lo_halves(vk[4][w], vk[5][w]);
-            a[3] = lo_halves(vk[6][w], vk[7][w]);
-          } else {
-            a[0] = hi_halves(vk[0][w], vk[1][w]);
-            a[1] = hi_halves(vk[2][w], vk[3][w]);
-            a[2] = hi_halves(vk[4][w], vk[5][w]);
-            a[3] = hi_halves(vk[6][w], vk[7][w]);
-          }
+          const u32x4 a = *(const u32x4*)(vt_rd + 32 * t * kVtPitch + 16 * (u ^ t));
           o[t] = mfma_32x32x16(a, pb[u], o[t]);
         }
       }
@@ -257,24 +299,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillKernelArgs p) {
   if (!row_ok) return;
   float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / ltot;
-  // Register i of tile t holds d = 32*(i/4) + 16*hgrp + 4*(i%4) + t: for fixed i/4
-  // the lane owns 16 contiguous d values.
+  // Register r of tile t holds d = 32t + 8*(r/4) + 4*hgrp + (r%4).
   uint16_t* dst = p.out + ((int64_t)(q_row0 + tok) * p.num_q_heads + (int64_t)g * G + hh) *
-                              kHeadDim + 16 * hgrp;
+                              kHeadDim + 4 * hgrp;
 #pragma unroll
-  for (int a4 = 0; a4 < 4; ++a4) {
-    u32x4 w0, w1;
-    // d offsets 0..7 -> (i%4 = 0, t=0..3), (i%4 = 1, t=0..3)
-    w0[0] = pack_bf16x2(o[0][4 * a4 + 0] * inv, o[1][4 * a4 + 0] * inv);
-    w0[1] = pack_bf16x2(o[2][4 * a4 + 0] * inv, o[3][4 * a4 + 0] * inv);
-    w0[2] = pack_bf16x2(o[0][4 * a4 + 1] * inv, o[1][4 * a4 + 1] * inv);
-    w0[3] = pack_bf16x2(o[2][4 * a4 + 1] * inv, o[3][4 * a4 + 1] * inv);
-    w1[0] = pack_bf16x2(o[0][4 * a4 + 2] * inv, o[1][4 * a4 + 2] * inv);
-    w1[1] = pack_bf16x2(o[2][4 * a4 + 2] * inv, o[3][4 * a4 + 2] * inv);
-    w1[2] = pack_bf16x2(o[0][4 * a4 + 3] * inv, o[1][4 * a4 + 3] * inv);
-    w1[3] = pack_bf16x2(o[2][4 * a4 + 3] * inv, o[3][4 * a4 + 3] * inv);
-    *(u32x4*)(dst + 32 * a4) = w0;
-    *(u32x4*)(dst + 32 * a4 + 8) = w1;
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      u32x2 w;
+      w[0] = pack_bf16x2(o[t][4 * a4 + 0] * inv, o[t][4 * a4 + 1] * inv);
+      w[1] = pack_bf16x2(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
+      *(u32x2*)(dst + 32 * t + 8 * a4) = w;
+    }
   }
 }
 
