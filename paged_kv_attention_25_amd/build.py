@@ -20,6 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpka.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip"]
+# Per-source flags (none at present).
+SOURCE_FLAGS = {}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -36,7 +38,8 @@ COMMON_FLAGS = [
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -536,10 +536,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   const size_t units = (size_t)a.batch * a.num_q_heads * plan.num_splits;
   k.part_o = (float*)a.workspace;
   k.part_lse = plan.num_splits > 1 ? k.part_o + units * kHeadDim : nullptr;
-  k.pg.page_size = a.page_size;
-  k.pg.page_shift = page_shift_of(a.page_size);
-  k.pg.num_pages = a.num_pages;
-  k.pg.table_width = a.pt_stride;
+  k.pg = make_page_geom(a.page_size, a.pt_stride, a.num_pages);
   k.pt_stride = a.pt_stride;
   k.batch = a.batch;
   k.num_q_heads = a.num_q_heads;

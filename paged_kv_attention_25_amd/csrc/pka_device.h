@@ -62,7 +62,32 @@ struct PageGeom {
   int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
   int32_t table_width;  // entries per page-table row
   int64_t num_pages;
+  uint32_t div_magic;   // key / page_size == (key * div_magic) >> div_shift, 0 <= key < 2^31
+  int32_t div_shift;
 };
+
+// Host: the geometry of a pool of `num_pages` pages of `page_size` slots read through
+// page-table rows of `table_width` entries. Division by the page size becomes a
+// multiply and a shift: with l = ceil(log2 P), shift = 31 + l and magic =
+// ceil(2^shift / P) < 2^32, the error magic*P - 2^shift is below P <= 2^l, so for
+// key < 2^31 it adds less than 1/P to key/P and the floor is exact.
+inline PageGeom make_page_geom(int32_t page_size, int32_t table_width, int64_t num_pages) {
+  PageGeom g;
+  g.page_size = page_size;
+  g.table_width = table_width;
+  g.num_pages = num_pages;
+  int32_t l = 0;
+  while ((int64_t(1) << l) < page_size) ++l;
+  g.page_shift = (int64_t(1) << l) == page_size ? l : -1;
+  g.div_shift = 31 + l;
+  g.div_magic = (uint32_t)(((uint64_t(1) << g.div_shift) + page_size - 1) / (uint64_t)page_size);
+  return g;
+}
+
+// Page-table index of logical token `key` (0 <= key < 2^31).
+__device__ __forceinline__ int32_t page_index(int32_t key, const PageGeom& pg) {
+  return (int32_t)(((uint64_t)(uint32_t)key * pg.div_magic) >> pg.div_shift);
+}
 
 // Slot of logical token `key` of the request whose page-table row is `row`, or -1
 // when the entry lies past the row or the page id is outside the pool (such a key

@@ -6,29 +6,33 @@
 // 6.1 and 6.5; keys located through page-table metadata: "miniSGLang intro blog",
 // section 1.3).
 //
-// Tiling. A workgroup of 4 wavefronts owns 128 query rows of one (request, kv head).
-// Rows are (token, head-in-group) pairs, row r = i*G + hh, so the G q heads that
-// share a kv head share every K/V tile. Each wavefront owns 32 rows. Keys are
-// processed in tiles of 64: the tile's K rows are gathered through the page table
-// into LDS row-major (272-byte pitch), its V rows transposed into LDS (V^T, one row
-// per d, 144-byte pitch, 16-byte chunks XOR-swizzled by row), with the next tile's
-// global loads in flight while the current tile is computed.
+// Tiling. A workgroup of 8 wavefronts (two per SIMD) owns 256 query rows of one
+// (request, kv head). Rows are (token, head-in-group) pairs, row r = i*G + hh, so the
+// G q heads that share a kv head share every K/V tile. Each wavefront owns 32 rows. Keys are
+// processed in tiles of 64, copied through the page table straight from the pool
+// into LDS (no registers in between): four stages, one barrier per tile, a tile's
+// loads issued about one and a half tiles before its first use. The page-table
+// entries the loads need are copied into LDS the same way two tiles earlier, so every
+// global access of the loop is one in-order stream with exact waits.
+//
+// LDS layout: K and V tiles are row-major (one 256-byte row per key) with the 16-byte
+// chunks of row r XOR-swizzled, by r % 16 for K and by 2*(r % 8) for V, so that the K
+// operand reads (16 bytes per lane) and the transposing V reads (8 bytes per lane)
+// spread over all banks.
 //
 // Per wavefront and tile, with 32x32x16 bf16 MFMAs:
-//   S^T[key][row] = K . Q^T   (A = K from LDS, B = Q held in registers)
-//   O^T[d][row]  += V^T . P^T (A = V^T from LDS, B = P^T straight from S^T's registers)
+//   S^T[key][row] = K . Q^T   (A = K rows from LDS, B = Q held in registers)
+//   O^T[d][row]  += V^T . P^T (A = V^T from LDS by transposing reads, B = P^T taken
+//                              straight from S^T's registers)
 // Index choices:
-//  * QK reduction order: lane l feeds d = 16c + 8*(l/32) + j to MFMA c, a 16-byte
-//    LDS read of K and a 16-byte global read of Q.
-//  * PV key order: MFMA u takes keys 16u + 8*(j/4) + 4*(l/32) + (j%4), which are
-//    exactly the scores lane l already holds, so P^T needs no data movement. V^T
-//    stores key k of a 16-key group at position k with bits 2 and 3 swapped, which
-//    makes those 8 keys contiguous: each V^T operand is one 16-byte LDS read.
+//  * QK reduction order: lane l feeds d = 16c + 8*(l/32) + j to MFMA c.
+//  * PV key order: MFMA u contracts the 16 keys 16u + 8*(j/4) + 4*(l/32) + (j%4),
+//    the scores lane l already holds, so P^T needs no data movement; the transposing
+//    reads fetch V rows in that order.
 // Softmax runs in the log2 domain with the scale folded into one FMA per score. The
 // running max is only raised (and the output rescaled) when it grows by more than
 // 2^8, so most tiles skip the rescale; probabilities stay below 2^8 in between.
-// Causal masking only on tiles that cross a wavefront's diagonal; tiles past the
-// last row's position are skipped.
+// Causal masking only on tiles that cross a wavefront's diagonal.
 #include "pka_device.h"
 #include "pka_kernels.h"
 
@@ -37,13 +41,19 @@ namespace pka {
 namespace {
 
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = 4;
-constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 128
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 256
+constexpr int kKeysPerWave = 8;                       // keys of a tile each wavefront loads
 constexpr int kKeysPerTile = 64;
-constexpr int kLdsPitch = kHeadDim + 8;     // K rows: elements; 272 bytes per row
-constexpr int kVtPitch = kKeysPerTile + 8;  // V^T rows: elements; 144 bytes per row
-constexpr float kRescaleLog2 = 8.f;         // raise the running max past 2^8 growth
+constexpr int kTileElems = kKeysPerTile * kHeadDim;   // one K or V tile: 16 KB
+constexpr int kStages = 4;  // power of two
+constexpr float kRescaleLog2 = 8.f;  // raise the running max past 2^8 growth
 constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct PrefillKernelArgs {
   const uint16_t* __restrict__ q;
@@ -61,19 +71,65 @@ struct PrefillKernelArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t tiles_per_seq;  // ceil(max_extend * G / 128)
+  int32_t tiles_per_seq;  // ceil(max_extend * G / 256)
   float scale_log2;
 };
 
-// Position of key k (0..63) of a tile in the V^T rows: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// Element offset of 16-byte chunk c (0..15) of key row r in a K (or V) tile.
+__device__ __forceinline__ int k_chunk(int r, int c) { return r * kHeadDim + 8 * (c ^ (r & 15)); }
+__device__ __forceinline__ int v_chunk(int r, int c) {
+  return r * kHeadDim + 8 * (c ^ (2 * (r & 7)));
 }
-// V^T row d keeps its eight 16-byte chunks XOR-swizzled by (d / 16) % 8, so that both
-// the transposing 8-byte writes and the 16-byte operand reads spread over all banks.
 
-// Two workgroups (8 wavefronts) per CU.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// Transposing LDS read: within each 16-lane group, lane i receives element i % 4 of
+// the four 8-byte chunks addressed by lanes 4j + i/4 (j = 0..3), in that order.
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Global -> LDS copies, no registers in between: lane l's 16 (or 4) bytes from `src`
+// land at `lds_dst` + 16*l (4*l); `lds_dst` is the same for the whole wavefront and
+// goes in M0 (one wait state before the load reads it). Completion is counted by
+// vmcnt like any other vector load. They are issued from inline assembly so that the
+// compiler adds no waits of its own before later LDS reads (it cannot tell the ring
+// stages apart); the kernel waits for exactly the copies it needs (wait_vmcnt) and
+// its own vmcnt waits stay correct, only more conservative, with these in flight.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void global_to_lds(const uint16_t* src, uint16_t* lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_address(lds_dst)) : "memory", "m0");
+}
+__device__ __forceinline__ void global_to_lds_b32(const int32_t* src, int32_t* lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_address(lds_dst)) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their
+  // maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence. The loads into LDS it orders are waited
+// for explicitly (wait_vmcnt) before it.
+__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// max(x of this lane, x of lane l ^ 32).
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Two wavefronts per SIMD: while one runs its MFMAs the other runs its softmax or
+// waits on LDS.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillKernelArgs p) {
   // Block id -> (q tile, request, kv head); the highest q tiles (the most keys)
   // are dispatched first, and with the kv head fastest all tiles of one
@@ -93,33 +149,32 @@ void prefill_kernel(PrefillKernelArgs p) {
   const int q_row0 = p.cu_extend[b];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int col = lane & 31;  // MFMA column: this lane's query row within the wave
-  const int hgrp = lane >> 5; // MFMA reduction group
+  const int col = lane & 31;   // MFMA column: this lane's query row
+  const int hgrp = lane >> 5;  // MFMA reduction group
 
   // Keys the block needs: 0 .. prefix + (token of its last row).
   const int last_row_blk = min(row0 + kRowsPerBlock, nrows) - 1;
   const int key_end = prefix + last_row_blk / G + 1;
+  const int n_tiles = (key_end + kKeysPerTile - 1) / kKeysPerTile;
 
   // This lane's query row.
   const int r = row0 + wave * kRowsPerWave + col;
   const bool row_in = r < nrows;
   const int tok = row_in ? r / G : 0;
-  const bool row_ok = row_in && q_row0 + tok >= 0 && q_row0 + tok < p.num_tokens;  // in bounds
   const int hh = row_in ? r - tok * G : 0;
+  const bool row_ok = row_in && q_row0 + tok >= 0 && q_row0 + tok < p.num_tokens;
   const int lim = prefix + tok;  // last visible key of this row
-  // The wave's smallest and largest limits (rows are in token order).
+  // The wavefront's smallest limit (rows are in token order).
   const int wrow_first = row0 + wave * kRowsPerWave;
-  const int wrow_last = min(wrow_first + kRowsPerWave, nrows) - 1;
-  const bool wave_live = wrow_first < nrows;
-  const int wave_lim_lo = prefix + (wave_live ? wrow_first / G : 0);
-  const int wave_lim_hi = prefix + (wave_live ? wrow_last / G : 0);
+  const int wave_lim_lo = prefix + (wrow_first < nrows ? wrow_first / G : 0);
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeysPerTile * kLdsPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVtPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kStages * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kStages * kTileElems];
+  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kStages][kWaves][64];
 
-  // Q^T operand: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
+  // Q^T operands: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
   u32x4 qv[8];
   if (row_ok) {
     const u32x4* src = (const u32x4*)(p.q + ((int64_t)(q_row0 + tok) * p.num_q_heads +
@@ -131,185 +186,187 @@ void prefill_kernel(PrefillKernelArgs p) {
     for (int c = 0; c < 8; ++c) qv[c] = u32x4{0, 0, 0, 0};
   }
 
-  // Global -> LDS staging: thread covers 16-byte chunk m = tid % 16 (d = 8m .. 8m+7)
-  // of the four keys 4a .. 4a+3, a = tid / 16.
+  // K/V tiles go from the pool straight into LDS (no registers in between). Wavefront
+  // w loads keys 8w .. 8w+7 of a tile: instruction i covers keys 8w + 4i + l/16, and
+  // lane l writes LDS bytes 16l .. 16l+15 of its 1 KB, i.e. chunk position l % 16 of
+  // key row 8w + 4i + l/16, so it fetches the chunk the swizzle puts there.
   const int64_t row_elems = (int64_t)p.num_kv_heads * kHeadDim;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_stride;
-  const int ld_m = tid & 15;
-  const int ld_a = tid >> 4;
-  const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim + 8 * ld_m;
-  const uint16_t* vbase = p.v_pool + (int64_t)g * kHeadDim + 8 * ld_m;
-  // Page-table entries of this thread's four keys of a tile are loaded one tile ahead
-  // of the K/V loads that use them, so no load waits on another in the loop. Every
-  // load is unconditional and in bounds: keys past the block's last key are clamped to
-  // it, a table index past the row to the row's last entry, and a page id outside the
-  // pool reads slot 0 (that request's result is then unspecified).
-  int32_t raw_page[4], raw_off[4];
-  auto lookup = [&](int kt) {
+  const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim;
+  const uint16_t* vbase = p.v_pool + (int64_t)g * kHeadDim;
+  // Key of instruction i of a tile starting at kt; keys past the block's last key are
+  // clamped to it (loaded, never used).
+  auto dma_key = [&](int kt, int i) {
+    return min(kt + kKeysPerWave * wave + 4 * i + (lane >> 4), key_end - 1);
+  };
+  // Page-table entries of a tile's keys also go straight into LDS, into a ring of
+  // kStages slots per wavefront: lane p (of the first 8) fetches the entry of the
+  // wavefront's key 4*(p%2) + p/2, so lane l later reads the entries of its two keys
+  // 4i + l/16 (i = 0, 1) as one 8-byte word at position 2*(l/16). A table index past
+  // the row reads the row's last entry.
+  auto ids_dma = [&](int kt, int slot) {
+    const int p8 = lane & 7;
+    const int key = min(kt + kKeysPerWave * wave + 4 * (p8 & 1) + (p8 >> 1), key_end - 1);
+    const int idx = min(page_index(key, p.pg), p.pg.table_width - 1);
+    global_to_lds_b32(pt_row + idx, &ids_lds[slot][wave][0]);
+  };
+  // Issue the K/V loads of the tile at kt into `stage` from its page-table entries in
+  // ring slot `slot`. A page id outside the pool reads slot 0 (that request's result
+  // is then unspecified); every access stays in bounds.
+  auto dma_tile = [&](int kt, int stage, int slot) {
+    const i32x2 page = *(const i32x2*)&ids_lds[slot][wave][2 * (lane >> 4)];
+    uint16_t* kd = k_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
+    uint16_t* vd = v_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(kt + 4 * ld_a + i, key_end - 1);
-      int idx;
-      if (p.pg.page_shift >= 0) {
-        idx = key >> p.pg.page_shift;
-        raw_off[i] = key & (p.pg.page_size - 1);
-      } else {
-        idx = key / p.pg.page_size;
-        raw_off[i] = key - idx * p.pg.page_size;
-      }
-      raw_page[i] = pt_row[min(idx, p.pg.table_width - 1)];
+    for (int i = 0; i < 2; ++i) {
+      const int key = dma_key(kt, i);
+      const int off = key - page_index(key, p.pg) * p.pg.page_size;
+      const int32_t slot_i =
+          (uint32_t)page[i] < (uint64_t)p.pg.num_pages ? page[i] * p.pg.page_size + off : 0;
+      const int64_t row = (int64_t)slot_i * row_elems;
+      const int rr = (kKeysPerWave * wave + 4 * i + (lane >> 4)) & 15;  // key row mod 16
+      global_to_lds(kbase + row + 8 * ((lane & 15) ^ rr), kd + 4 * i * kHeadDim);
+      global_to_lds(vbase + row + 8 * ((lane & 15) ^ (2 * (rr & 7))), vd + 4 * i * kHeadDim);
     }
   };
-  u32x4 kst[4], vst[4];
-  auto load_tile = [&]() {
+
+  // K operand reads: row 32*kb2 + col, chunk 2c + hgrp (swizzled by col % 16).
+  int k_rd[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hold(raw_page[i]);
-      const int32_t page = raw_page[i];
-      const int32_t slot =
-          (uint32_t)page < (uint64_t)p.pg.num_pages ? page * p.pg.page_size + raw_off[i] : 0;
-      kst[i] = *(const u32x4*)(kbase + (int64_t)slot * row_elems);
-      vst[i] = *(const u32x4*)(vbase + (int64_t)slot * row_elems);
-    }
-  };
-  // K: row-major, key row at 272-byte pitch.
-  uint16_t* const k_st = k_lds + 4 * ld_a * kLdsPitch + 8 * ld_m;
-  // V^T: row d = 8m + j; the four keys land at positions vt_pos(4a) .. +3 of 16-byte
-  // chunk c = vt_pos(4a)/8, stored at chunk c ^ vt_swz(d) (8 bytes per row and key quad).
-  const int vq = vt_pos(4 * ld_a);
-  uint16_t* const vt_st = vt_lds + 8 * ld_m * kVtPitch + 8 * ((vq >> 3) ^ (ld_m >> 1)) + (vq & 7);
-  auto store_tile = [&]() {
+  for (int c = 0; c < 8; ++c) k_rd[c] = k_chunk(col, 2 * c + hgrp);
+  // V^T operand reads for d block t4 (d = 32*t4 + l % 32), key chunk u, half h: lane
+  // (group gq = l/16, s = l%16) addresses key 16u + 8h + 4*(gq/2) + s/4 at
+  // d = 32*t4 + 16*(gq%2) + 4*(s%4); the key part 16u + 8h is a whole number of rows.
+  const int gq = lane >> 4;
+  const int sq = lane & 15;
+  int v_rd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(k_st + i * kLdsPitch) = kst[i];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x2 lo, hi;  // d = 8m + 2w and 8m + 2w + 1, keys 4a .. 4a+3
-      lo[0] = lo_halves(vst[0][w], vst[1][w]);
-      lo[1] = lo_halves(vst[2][w], vst[3][w]);
-      hi[0] = hi_halves(vst[0][w], vst[1][w]);
-      hi[1] = hi_halves(vst[2][w], vst[3][w]);
-      *(u32x2*)(vt_st + (2 * w) * kVtPitch) = lo;
-      *(u32x2*)(vt_st + (2 * w + 1) * kVtPitch) = hi;
-    }
-  };
-  // PV operand read base: V^T row col (+32t), chunk (2u + hgrp) ^ vt_swz(32t + col)
-  // = 2(u ^ t) + (hgrp ^ (col / 16)).
-  const uint16_t* const vt_rd = vt_lds + col * kVtPitch + 8 * (hgrp ^ (col >> 4));
+  for (int t4 = 0; t4 < 4; ++t4) {
+    const int rv = 4 * (gq >> 1) + (sq >> 2);
+    const int d = 32 * t4 + 16 * (gq & 1) + 4 * (sq & 3);
+    v_rd[t4] = v_chunk(rv, d >> 3) + (d & 7);
+  }
 
   float m = kNegInf;
   float lsum = 0.f;
   f32x16 o[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+    for (int i = 0; i < 16; ++i) o[t4][i] = 0.f;
 
-  lookup(0);
-  load_tile();
-  store_tile();
-  lookup(kKeysPerTile);
-  __syncthreads();
+  // Prologue: page-table entries of tiles 0..4 and the K/V of tiles 0..2 loaded.
+#pragma unroll
+  for (int t = 0; t < 3; ++t) ids_dma(t * kKeysPerTile, t);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int t = 0; t < 3; ++t) dma_tile(t * kKeysPerTile, t, t);
+  ids_dma(3 * kKeysPerTile, 3);
+  ids_dma(4 * kKeysPerTile, 0);
+  wait_vmcnt<0>();
+  lds_barrier();
 
-  for (int kt = 0; kt < key_end; kt += kKeysPerTile) {
-    const bool has_next = kt + kKeysPerTile < key_end;
-    // Next tile's K/V and the page ids of the one after (past the end: clamped reloads).
-    load_tile();
-    lookup(kt + 2 * kKeysPerTile);
+  f32x16 s[2];  // S^T of the current tile: two 32-key blocks
+  u32x4 pb[4];  // P^T operands, one per 16-key chunk
 
-    if (wave_live && kt <= wave_lim_hi) {
-      // S^T for two 32-key blocks.
-      f32x16 sblk[2];
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kt = t * kKeysPerTile;
+    const int stage = t & (kStages - 1);
+    const uint16_t* kt_lds = k_lds + stage * kTileElems;
+    const uint16_t* vt_lds = v_lds + stage * kTileElems;
+
+    // S^T = K Q^T for the tile's two 32-key blocks.
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sblk[kb2][i] = 0.f;
-        const uint16_t* krow = k_lds + (kb2 * 32 + col) * kLdsPitch + 8 * hgrp;
+      for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const u32x4 a = *(const u32x4*)(krow + 16 * c);
-          sblk[kb2] = mfma_32x32x16(a, qv[c], sblk[kb2]);
-        }
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 a = *(const u32x4*)(kt_lds + 32 * kb2 * kHeadDim + k_rd[c]);
+        s[kb2] = mfma_32x32x16(a, qv[c], s[kb2]);
       }
-      // Causal mask only where the tile crosses this wavefront's diagonal: register i
-      // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
-      if (kt + kKeysPerTile - 1 > wave_lim_lo) {
-        const int dl = lim - kt - 4 * hgrp;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) sblk[kb2][i] = kNegInf;
-      }
-      float mx = kNegInf;
+    }
+    // Causal mask only where the tile crosses this wavefront's diagonal: register i
+    // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
+    if (kt + kKeysPerTile - 1 > wave_lim_lo) {
+      const int dl = lim - kt - 4 * hgrp;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sblk[kb2][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Raw-score max; the scale is applied inside the exponent. Rescale only when
-      // some row's max grew by more than 2^kRescaleLog2 (or has no value yet).
-      const bool grow = (mx - m) * p.scale_log2 > kRescaleLog2;
-      if (__any(grow)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
-        lsum *= alpha;
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) s[kb2][i] = kNegInf;
+    }
+    float mx = kNegInf;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) o[t] = o[t] * alpha;
-        m = m_new;
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+    mx = max_across_halves(mx);
+    // Raw-score max; the scale is applied inside the exponent. Rescale only when
+    // some row's max grew by more than 2^kRescaleLog2 (or has no value yet).
+    const bool grow = (mx - m) * p.scale_log2 > kRescaleLog2;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) o[t4] = o[t4] * alpha;
+      m = m_new;
+    }
+    const float neg_m = -m * p.scale_log2;
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float pr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
+        ps += pr[j];
       }
-      const float neg_m = (m == kNegInf) ? 0.f : -m * p.scale_log2;
-      float ps = 0.f;
-      u32x4 pb[4];  // P^T operands for the 4 PV MFMAs (16 keys each)
+      pb[u][0] = pack_bf16x2(pr[0], pr[1]);
+      pb[u][1] = pack_bf16x2(pr[2], pr[3]);
+      pb[u][2] = pack_bf16x2(pr[4], pr[5]);
+      pb[u][3] = pack_bf16x2(pr[6], pr[7]);
+    }
+    lsum += ps;
+    // O^T += V^T P^T: d block t4, 16-key chunk u.
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kb2 = u >> 1;
-        const int r0 = 8 * (u & 1);
-        float pr[8];
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pr[j] = fast_exp2(fmaf(sblk[kb2][r0 + j], p.scale_log2, neg_m));
-          ps += pr[j];
-        }
-        pb[u][0] = pack_bf16x2(pr[0], pr[1]);
-        pb[u][1] = pack_bf16x2(pr[2], pr[3]);
-        pb[u][2] = pack_bf16x2(pr[4], pr[5]);
-        pb[u][3] = pack_bf16x2(pr[6], pr[7]);
-      }
-      lsum += ps;
-
-      // O^T += V^T P^T: tile t covers d = 32t .. 32t+31; MFMA u takes the 16 keys at
-      // V^T positions 16u .. 16u+15, lane group hgrp the 8 at 16u + 8*hgrp.
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u32x4 a = *(const u32x4*)(vt_rd + 32 * t * kVtPitch + 16 * (u ^ t));
-          o[t] = mfma_32x32x16(a, pb[u], o[t]);
-        }
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const uint16_t* src = vt_lds + 16 * u * kHeadDim + v_rd[t4];
+        const u32x2 lo = tr_read(src);
+        const u32x2 hi = tr_read(src + 8 * kHeadDim);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        o[t4] = mfma_32x32x16(a, pb[u], o[t4]);
       }
     }
 
-    if (has_next) {
-      __syncthreads();  // every wave is done reading this tile
-      store_tile();
-      __syncthreads();
-    }
+    // Tile t+1 and the page-table entries of tile t+3 have landed: issued after them
+    // are at most the 4 loads of tile t+2 and the entries of tile t+4 (one load). The
+    // barrier also shows every wavefront is done with tile t-1, whose stage the loads
+    // of tile t+3 reuse.
+    wait_vmcnt<5>();
+    lds_barrier();
+    if (t + 3 < n_tiles)
+      dma_tile(kt + 3 * kKeysPerTile, (t + 3) & (kStages - 1), (t + 3) & (kStages - 1));
+    if (t + 5 < n_tiles) ids_dma(kt + 5 * kKeysPerTile, (t + 5) & (kStages - 1));
   }
 
   if (!row_ok) return;
-  float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / ltot;
-  // Register r of tile t holds d = 32t + 8*(r/4) + 4*hgrp + (r%4).
+  // Register r of tile t4 holds d = 32*t4 + 8*(r/4) + 4*hgrp + (r%4).
   uint16_t* dst = p.out + ((int64_t)(q_row0 + tok) * p.num_q_heads + (int64_t)g * G + hh) *
                               kHeadDim + 4 * hgrp;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       u32x2 w;
-      w[0] = pack_bf16x2(o[t][4 * a4 + 0] * inv, o[t][4 * a4 + 1] * inv);
-      w[1] = pack_bf16x2(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
-      *(u32x2*)(dst + 32 * t + 8 * a4) = w;
+      w[0] = pack_bf16x2(o[t4][4 * a4 + 0] * inv, o[t4][4 * a4 + 1] * inv);
+      w[1] = pack_bf16x2(o[t4][4 * a4 + 2] * inv, o[t4][4 * a4 + 3] * inv);
+      *(u32x2*)(dst + 32 * t4 + 8 * a4) = w;
     }
   }
 }
@@ -327,10 +384,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   k.extend_lens = a.extend_lens;
   k.cu_extend = a.cu_extend;
   k.out = (uint16_t*)a.out;
-  k.pg.page_size = a.page_size;
-  k.pg.page_shift = page_shift_of(a.page_size);
-  k.pg.num_pages = a.num_pages;
-  k.pg.table_width = a.pt_stride;
+  k.pg = make_page_geom(a.page_size, a.pt_stride, a.num_pages);
   k.pt_stride = a.pt_stride;
   k.batch = a.batch;
   k.num_tokens = a.num_tokens;
@@ -341,7 +395,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   k.tiles_per_seq = (int32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
   k.scale_log2 = a.scale * kLog2e;
   const int64_t blocks = (int64_t)k.tiles_per_seq * a.batch * a.num_kv_heads;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, k);
   return hipGetLastError();
 }
 
