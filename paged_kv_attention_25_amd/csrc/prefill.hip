@@ -343,10 +343,15 @@ void prefill_kernel(PrefillKernelArgs p) {
     }
 
     // Tile t+1 and the page-table entries of tile t+3 have landed: issued after them
-    // are at most the 4 loads of tile t+2 and the entries of tile t+4 (one load). The
-    // barrier also shows every wavefront is done with tile t-1, whose stage the loads
-    // of tile t+3 reuse.
-    wait_vmcnt<5>();
+    // are the 4 loads of tile t+2 and the entries of tile t+4 (one load), each only if
+    // that tile exists. The barrier also shows every wavefront is done with tile t-1,
+    // whose stage the loads of tile t+3 reuse.
+    if (t + 4 < n_tiles)
+      wait_vmcnt<5>();
+    else if (t + 2 < n_tiles)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
     lds_barrier();
     if (t + 3 < n_tiles)
       dma_tile(kt + 3 * kKeysPerTile, (t + 3) & (kStages - 1), (t + 3) & (kStages - 1));
