@@ -120,6 +120,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // for explicitly (wait_vmcnt) before it.
 __device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Instruction-scheduling hints: ask for a group of `n` instructions of one kind at
+// this point of the scheduling region (groups are placed in program order).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+#define sched_group(kind, n) __builtin_amdgcn_sched_group_barrier((kind), (n), 0)
+
 // max(x of this lane, x of lane l ^ 32).
 __device__ __forceinline__ float max_across_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -275,7 +281,8 @@ void prefill_kernel(PrefillKernelArgs p) {
     const uint16_t* kt_lds = k_lds + stage * kTileElems;
     const uint16_t* vt_lds = v_lds + stage * kTileElems;
 
-    // S^T = K Q^T for the tile's two 32-key blocks.
+    // S^T = K Q^T for the tile's two 32-key blocks. The K operands are read 8 MFMAs
+    // ahead of their use (the schedule below), so LDS latency stays hidden.
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -286,6 +293,13 @@ void prefill_kernel(PrefillKernelArgs p) {
         s[kb2] = mfma_32x32x16(a, qv[c], s[kb2]);
       }
     }
+    sched_group(kSchedDsRead, 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sched_group(kSchedMfma, 1);
+      sched_group(kSchedDsRead, 1);
+    }
+    sched_group(kSchedMfma, 8);
     // Causal mask only where the tile crosses this wavefront's diagonal: register i
     // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
     if (kt + kKeysPerTile - 1 > wave_lim_lo) {
@@ -329,7 +343,8 @@ void prefill_kernel(PrefillKernelArgs p) {
       pb[u][3] = pack_bf16x2(pr[6], pr[7]);
     }
     lsum += ps;
-    // O^T += V^T P^T: d block t4, 16-key chunk u.
+    // O^T += V^T P^T: d block t4, 16-key chunk u; the V^T operands are read 4 MFMAs
+    // ahead of their use.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -341,6 +356,13 @@ void prefill_kernel(PrefillKernelArgs p) {
         o[t4] = mfma_32x32x16(a, pb[u], o[t4]);
       }
     }
+    sched_group(kSchedDsRead, 8);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      sched_group(kSchedMfma, 1);
+      sched_group(kSchedDsRead, 2);
+    }
+    sched_group(kSchedMfma, 4);
 
     // Tile t+1 and the page-table entries of tile t+3 have landed: issued after them
     // are the 4 loads of tile t+2 and the entries of tile t+4 (one load), each only if
