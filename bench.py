@@ -189,6 +189,72 @@ def traffic_for(kernel_hash):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 512 << 20   # the calibration copy: 512 MiB read, 512 MiB written
+
+
+def _dispatch_counters(csv_dir, counter):
+    """Per-dispatch values of one counter from a rocprofv3 counter_collection.csv:
+    {kernel name: [(value, grid size) per dispatch, ...]}."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"], int(r["Grid_Size"]))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _, grid), v in per.items():
+        out.setdefault(name, []).append((v, grid))
+    return out
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per decode launch on decode_b256 from two counter runs of
+    `bench.py --quick --calibration-copy` (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch). Each counter is scaled by what it reads for the 512 MiB copy."""
+    fetch = _dispatch_counters(fetch_dir, "FETCH_SIZE")
+    write = _dispatch_counters(write_dir, "WRITE_SIZE")
+
+    def mean_of(d, tag, largest_grid=False):
+        vals = [vg for name, vs in d.items() if tag in name for vg in vs]
+        if largest_grid:   # the 512 MiB copies, not the small metadata uploads
+            g = max(grid for _, grid in vals) if vals else 0
+            vals = [(v, grid) for v, grid in vals if grid == g]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named *{tag}*")
+        return sum(v for v, _ in vals) / len(vals)
+
+    kib = 1024.0
+    fetch_scale = COPY_BYTES / (mean_of(fetch, "copyBuffer", True) * kib)
+    write_scale = COPY_BYTES / (mean_of(write, "copyBuffer", True) * kib)
+    f_split, f_merge = mean_of(fetch, "decode_split_kernel"), mean_of(fetch, "decode_merge_kernel")
+    w_split, w_merge = mean_of(write, "decode_split_kernel"), mean_of(write, "decode_merge_kernel")
+    total = ((f_split + f_merge) * fetch_scale + (w_split + w_merge) * write_scale) * kib
+    rec = {"source_hash": source_hash("decode.hip", "pka_device.h"), "workload": "decode_b256",
+           "kernels": "decode_split_kernel + decode_merge_kernel",
+           "bytes_per_launch": int(round(total)),
+           "fetch_kib": {"split": round(f_split, 1), "merge": round(f_merge, 1)},
+           "write_kib": {"split": round(w_split, 1), "merge": round(w_merge, 1)},
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+           "calibration": "rocclr copyBuffer of 512 MiB in the same process",
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- "
+                        "python3 bench.py --quick --steps 3 --warmup 1 --no-cpu-baseline "
+                        "--calibration-copy",
+                        "rocprofv3 --pmc WRITE_SIZE -d <write_dir> --output-format csv -- "
+                        "python3 bench.py --quick --steps 3 --warmup 1 --no-cpu-baseline "
+                        "--calibration-copy",
+                        "python3 bench.py --traffic-from <fetch_dir> <write_dir>"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,7 +263,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--hot", action="store_true", help="also report hot-cache times")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run two 512 MiB device copies (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the decode_b256 traffic record from two counter runs, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
@@ -252,6 +325,14 @@ def main():
                    "wall_s_timed_region_incl_flush": round(wall, 4)},
         "roofline": roofline,
     }
+    if args.calibration_copy:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            flush()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.hot:
         seg_h, tot_h, _ = time_step(run, args.steps, 0, flush, cold=False)
         result["config"]["hot_cache_decode_GBs"] = round(dec_bytes / (seg_h[1] * 1e-3) / 1e9, 1)
