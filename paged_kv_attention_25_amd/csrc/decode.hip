@@ -429,7 +429,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // One wavefront per (request, q head): the split weights are computed once (lane s
-// holds split s), then lane l combines d = 2l, 2l+1 over the splits, four at a time.
+// holds split s), then lane l combines d = 2l, 2l+1 over the splits, 16 at a time.
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ seq_lens,
@@ -455,7 +455,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     wsum += w_l;
     const int cnt = min(64, nsplit - s0);
     const float* src = part_o + (unit0 + s0) * kHeadDim + 2 * lane;
+    // 16 splits' loads in flight at a time: a long row's merge is a chain of
+    // dependent memory latencies otherwise.
     int s = 0;
+    for (; s + 16 <= cnt; s += 16) {
+      float2 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = *(const float2*)(src + (int64_t)(s + i) * kHeadDim);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float w = __shfl(w_l, s + i);
+        acc0 += w * v[i].x;
+        acc1 += w * v[i].y;
+      }
+    }
     for (; s + 4 <= cnt; s += 4) {
       float2 v[4];
 #pragma unroll
