@@ -101,6 +101,11 @@ class Runner:
             else:
                 m.update(pre=i32(part.prefix_lens), ext=i32(part.extend_lens),
                          cu=i32(part.cu_extend))
+                need = pka.prefill_workspace_bytes(step.num_q_heads, step.num_kv_heads,
+                                                   step.head_dim, step.page_size,
+                                                   step.num_pages, part.batch, part.num_tokens,
+                                                   part.max_extend)
+                m["ws"] = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
             m["out"] = torch.empty_like(part.q)
             self.meta.append(m)
 
@@ -117,7 +122,7 @@ class Runner:
         else:
             self.pka.paged_attn_prefill(part.q, s.k_pool, s.v_pool, m["pt"], m["seq"], m["pre"],
                                         m["ext"], m["cu"], part.max_extend, part.max_seq_len,
-                                        s.page_size, s.scale, out=m["out"])
+                                        s.page_size, s.scale, out=m["out"], workspace=m["ws"])
 
 
 def time_step(runner, steps, warmup, flush, cold=True):

@@ -157,6 +157,8 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
  *   out           [num_tokens, Hq, D] bf16 (device)
  *   workspace     device scratch of at least
  *                 pka_prefill_workspace_bytes(geom, batch, num_tokens, max_extend) bytes
+ *                 (may be NULL when that size is 0); it holds the dispatch order of the
+ *                 launch's work items, written by the launch itself
  * Supported: D == 128. Requests with e_b == 0 produce no rows. batch == 0 or
  * num_tokens == 0 is a no-op.
  */
@@ -168,7 +170,9 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
                            int32_t max_extend, int32_t max_seq_len, float scale, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pka_paged_attn_prefill needs (0 for the current kernels). */
+/* Workspace bytes pka_paged_attn_prefill needs: 4 bytes per (request, 256-row q
+ * tile) item when batch > 1 (the launch orders its work heaviest first there), else 0.
+ * Contents on entry are ignored; calls that run concurrently must not share it. */
 size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,
                                    int32_t max_extend);
 

@@ -113,11 +113,9 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
 
 size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,
                                    int32_t max_extend) {
-  (void)geom;
-  (void)batch;
   (void)num_tokens;
-  (void)max_extend;
-  return 0;
+  if (!geom || !geom_ok(geom) || batch < 0 || max_extend < 0) return 0;
+  return pka::prefill_workspace_bytes(batch, geom->num_q_heads / geom->num_kv_heads, max_extend);
 }
 
 int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_pool,
@@ -127,8 +125,6 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
                            const int32_t* cu_extend, int32_t batch, int32_t num_tokens,
                            int32_t max_extend, int32_t max_seq_len, float scale, void* out,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!geom) return PKA_E_NULLPTR;
   const int gs = attn_geom_status(geom);
   if (gs != PKA_OK) return gs;
@@ -146,6 +142,8 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !prefix_lens || !extend_lens ||
       !cu_extend || !out)
     return PKA_E_NULLPTR;
+  const size_t need = pka::prefill_workspace_bytes(batch, (int32_t)group, max_extend);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKA_E_WORKSPACE;
   pka::PrefillArgs a;
   a.q = q;
   a.k_pool = k_pool;
@@ -165,6 +163,7 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
   a.num_q_heads = geom->num_q_heads;
   a.num_kv_heads = geom->num_kv_heads;
   a.scale = scale;
+  a.workspace = need > 0 ? workspace : nullptr;
   return launch_status(pka::launch_prefill(a, as_stream(stream)));
 }
 

@@ -69,7 +69,12 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   float scale;
+  void* workspace;  // prefill_workspace_bytes(...) bytes (dispatch order), may be null when 0
 };
+// Workspace of a prefill launch: the dispatch order of its (request, q tile) items,
+// one int32 each, when there is more than one request (a single request's items are
+// already dispatched heaviest first); 0 otherwise.
+size_t prefill_workspace_bytes(int32_t batch, int32_t group, int32_t max_extend);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 inline int32_t page_shift_of(int32_t page_size) {

@@ -73,7 +73,79 @@ struct PrefillKernelArgs {
   int32_t group;
   int32_t tiles_per_seq;  // ceil(max_extend * G / 256)
   float scale_log2;
+  const int32_t* __restrict__ schedule;  // item order (heaviest first), or null
 };
+
+// Work item r (0 .. tiles_per_seq*batch-1) is q tile tiles_per_seq-1 - r/batch of request
+// r % batch; with no schedule, items go out in that order (the highest q tiles, with
+// the most keys, first) and the kv head varies fastest across consecutive blocks.
+__device__ __forceinline__ int item_tiles(int item, const int32_t* __restrict__ prefix_lens,
+                                          const int32_t* __restrict__ extend_lens, int batch,
+                                          int group, int tiles_per_seq) {
+  const int b = item % batch;
+  const int tile = tiles_per_seq - 1 - item / batch;
+  const int nrows = extend_lens[b] * group;
+  const int row0 = tile * kRowsPerBlock;
+  if (row0 >= nrows) return 0;
+  const int key_end = prefix_lens[b] + (min(row0 + kRowsPerBlock, nrows) - 1) / group + 1;
+  return (key_end + kKeysPerTile - 1) / kKeysPerTile;
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 4096;  // work beyond 4095 tiles shares the last bin
+
+// Dispatch order for several requests: one workgroup counting-sorts the work items by
+// their number of key tiles, heaviest first (longest-processing-time-first list
+// scheduling onto the CUs), so that long items do not start last and leave a tail.
+// The order of items with equal work is arbitrary; it only affects timing.
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens,
+    int32_t batch, int32_t group, int32_t tiles_per_seq, int32_t* __restrict__ schedule) {
+  __shared__ int32_t start[kPlanBins];  // histogram, then first position of each bin
+  __shared__ int32_t wave_tot[kPlanThreads / 64];
+  const int tid = threadIdx.x;
+  const int items = tiles_per_seq * batch;
+  for (int i = tid; i < kPlanBins; i += kPlanThreads) start[i] = 0;
+  __syncthreads();
+  for (int it = tid; it < items; it += kPlanThreads) {
+    const int w = min(item_tiles(it, prefix_lens, extend_lens, batch, group, tiles_per_seq),
+                      kPlanBins - 1);
+    atomicAdd(&start[w], 1);
+  }
+  __syncthreads();
+  // Exclusive scan in descending work: thread t owns bins 4095-4t .. 4092-4t.
+  constexpr int kPer = kPlanBins / kPlanThreads;
+  int cnt[kPer];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    cnt[j] = start[kPlanBins - 1 - (kPer * tid + j)];
+    local += cnt[j];
+  }
+  int incl = local;  // inclusive scan across the wavefront
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_tot[tid >> 6] = incl;
+  __syncthreads();
+  int before = incl - local;
+  for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    start[kPlanBins - 1 - (kPer * tid + j)] = before;
+    before += cnt[j];
+  }
+  __syncthreads();
+  for (int it = tid; it < items; it += kPlanThreads) {
+    const int w = min(item_tiles(it, prefix_lens, extend_lens, batch, group, tiles_per_seq),
+                      kPlanBins - 1);
+    schedule[atomicAdd(&start[w], 1)] = it;
+  }
+}
 
 // Element offset of 16-byte chunk c (0..15) of key row r in a K (or V) tile.
 __device__ __forceinline__ int k_chunk(int r, int c) { return r * kHeadDim + 8 * (c ^ (r & 15)); }
@@ -137,12 +209,11 @@ __device__ __forceinline__ float max_across_halves(float x) {
 // waits on LDS.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillKernelArgs p) {
-  // Block id -> (q tile, request, kv head); the highest q tiles (the most keys)
-  // are dispatched first, and with the kv head fastest all tiles of one
-  // (request, kv head) land on the same XCD when the head count divides 8.
+  // Block id -> (work item, kv head), kv head fastest (all heads of an item run
+  // together); the item comes from the schedule when there is one.
   const int id = blockIdx.x;
   const int g = id % p.num_kv_heads;
-  const int rest = id / p.num_kv_heads;
+  const int rest = p.schedule ? p.schedule[id / p.num_kv_heads] : id / p.num_kv_heads;
   const int b = rest % p.batch;
   const int tile = p.tiles_per_seq - 1 - rest / p.batch;
 
@@ -400,6 +471,12 @@ void prefill_kernel(PrefillKernelArgs p) {
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int32_t batch, int32_t group, int32_t max_extend) {
+  if (batch <= 1 || max_extend <= 0 || group <= 0) return 0;
+  const int64_t tiles = ((int64_t)max_extend * group + kRowsPerBlock - 1) / kRowsPerBlock;
+  return (size_t)(tiles * batch) * sizeof(int32_t);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.num_tokens == 0 || a.max_extend == 0) return hipSuccess;
   PrefillKernelArgs k;
@@ -421,6 +498,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_extend * k.group;
   k.tiles_per_seq = (int32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
   k.scale_log2 = a.scale * kLog2e;
+  k.schedule = nullptr;
+  if (prefill_workspace_bytes(a.batch, k.group, a.max_extend) > 0) {
+    int32_t* sched = (int32_t*)a.workspace;
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.prefix_lens,
+                       a.extend_lens, a.batch, k.group, k.tiles_per_seq, sched);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k.schedule = sched;
+  }
   const int64_t blocks = (int64_t)k.tiles_per_seq * a.batch * a.num_kv_heads;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, k);
   return hipGetLastError();

@@ -64,10 +64,11 @@ def decode(L, g, batch=4, max_seq=250, stride=256, ws=None, ws_bytes=0, q=FAKE):
                                    None)
 
 
-def prefill(L, g, batch=2, tokens=10, max_ext=6, max_seq=20, stride=20, q=FAKE):
+def prefill(L, g, batch=2, tokens=10, max_ext=6, max_seq=20, stride=20, q=FAKE, ws=None,
+            ws_bytes=0):
     return L.pka_paged_attn_prefill(ctypes.byref(g) if g is not None else None, q, FAKE, FAKE,
                                     FAKE, stride, FAKE, FAKE, FAKE, FAKE, batch, tokens, max_ext,
-                                    max_seq, 0.1, FAKE, None, 0, None)
+                                    max_seq, 0.1, FAKE, ws, ws_bytes, None)
 
 
 def test_workspace_sizes(L):
@@ -78,7 +79,11 @@ def test_workspace_sizes(L):
     n = L.pka_decode_workspace_bytes(ctypes.byref(g), 32, 32768)
     assert n > 0 and n % (129 * 4) == 0
     assert L.pka_decode_workspace_bytes(None, 4, 100) == 0
-    assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 2, 10, 6) == 0
+    # prefill: one int32 per (request, 256-row q tile) item when batch > 1, else 0
+    assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 1, 10, 6) == 0
+    g40 = geom(num_q_heads=40, num_kv_heads=8)                      # G = 5
+    assert L.pka_prefill_workspace_bytes(ctypes.byref(g40), 32, 8192, 700) == 4 * 32 * 14
+    assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 2, 10, 6) == 4 * 2 * 1
 
 
 def test_decode_argument_errors(L):
@@ -106,6 +111,9 @@ def test_prefill_argument_errors(L):
     assert prefill(L, geom(), max_seq=5) == pka.PKA_E_SHAPE       # max_seq < max_extend
     assert prefill(L, geom(), stride=3) == pka.PKA_E_SHAPE
     assert prefill(L, geom(), q=None) == pka.PKA_E_NULLPTR
+    # several requests need the dispatch-order workspace
+    assert prefill(L, geom()) == pka.PKA_E_WORKSPACE
+    assert prefill(L, geom(), ws=FAKE, ws_bytes=4) == pka.PKA_E_WORKSPACE
     assert prefill(L, geom(), tokens=0) == pka.PKA_OK
     assert prefill(L, geom(), batch=0) == pka.PKA_OK
 
