@@ -128,8 +128,9 @@ class Runner:
 def time_step(runner, steps, warmup, flush, cold=True):
     """Run warmup steps, then `steps` timed steps. Each timed step records HIP events
     between its calls (store, then each attention part) on the current stream; a cache
-    flush runs before each timed step, outside the events. Returns per-segment mean ms,
-    total mean ms and the wall time of the bracketed region."""
+    flush runs before each timed step, outside the events. Returns the per-segment
+    median ms over the timed steps, their sum, and the wall time of the bracketed
+    region."""
     import torch
     nparts = len(runner.step.parts)
     for _ in range(warmup):
@@ -151,11 +152,8 @@ def time_step(runner, steps, warmup, flush, cold=True):
             e[i + 2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = np.zeros(nparts + 1)
-    for e in evs:
-        for j in range(nparts + 1):
-            seg[j] += e[j].elapsed_time(e[j + 1])
-    seg /= steps
+    per_step = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nparts + 1)] for e in evs])
+    seg = np.median(per_step, axis=0)
     return seg, float(seg.sum()), wall
 
 
@@ -326,7 +324,8 @@ def main():
                                "context U[200,2048], page_size 1, 2^20-slot pool; "
                                "step = store_kv(256) + split decode + merge",
                    "batch": part.batch, "sum_context": int(part.seq_lens.sum()),
-                   "timing": "HIP events on the launch stream, caches flushed before each step",
+                   "timing": "HIP events on the launch stream, caches flushed before each step; "
+                             "median over the timed steps",
                    "wall_s_timed_region_incl_flush": round(wall, 4)},
         "roofline": roofline,
     }
