@@ -10,10 +10,11 @@
 // (request, kv head). Rows are (token, head-in-group) pairs, row r = i*G + hh, so the
 // G q heads that share a kv head share every K/V tile. Each wavefront owns 32 rows. Keys are
 // processed in tiles of 64, copied through the page table straight from the pool
-// into LDS (no registers in between): four stages, one barrier per tile, a tile's
-// loads issued about one and a half tiles before its first use. The page-table
-// entries the loads need are copied into LDS the same way two tiles earlier, so every
-// global access of the loop is one in-order stream with exact waits.
+// into LDS (no registers in between) by four of the wavefronts: four stages, one
+// barrier per tile, a tile's loads issued between two and three tiles before its first
+// use. The page-table entries the loads need are copied into LDS the same way two
+// tiles earlier, so every global access of the loop is one in-order stream per loader
+// with exact waits.
 //
 // LDS layout: K and V tiles are row-major (one 256-byte row per key) with the 16-byte
 // chunks of row r XOR-swizzled, by r % 16 for K and by 2*(r % 8) for V, so that the K
@@ -44,15 +45,16 @@ constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 256
-constexpr int kKeysPerWave = 8;                       // keys of a tile each wavefront loads
 constexpr int kKeysPerTile = 64;
+constexpr int kLoaders = kWaves / 2;                   // wavefronts that load tiles
+constexpr int kKeysPerWave = kKeysPerTile / kLoaders;  // keys of a tile each loader loads
 constexpr int kTileElems = kKeysPerTile * kHeadDim;   // one K or V tile: 16 KB
 constexpr int kStages = 4;  // power of two
 constexpr float kRescaleLog2 = 8.f;  // raise the running max past 2^8 growth
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct PrefillKernelArgs {
@@ -249,7 +251,7 @@ void prefill_kernel(PrefillKernelArgs p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kStages * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kStages * kTileElems];
-  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kStages][kWaves][64];
+  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kStages][kLoaders][64];
 
   // Q^T operands: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
   u32x4 qv[8];
@@ -262,11 +264,17 @@ void prefill_kernel(PrefillKernelArgs p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) qv[c] = u32x4{0, 0, 0, 0};
   }
+  // Q has landed before any copy into LDS is issued: the compiler does not see those
+  // copies, so a wait it placed for Q later on would also wait for them.
+  wait_vmcnt<0>();
 
-  // K/V tiles go from the pool straight into LDS (no registers in between). Wavefront
-  // w loads keys 8w .. 8w+7 of a tile: instruction i covers keys 8w + 4i + l/16, and
-  // lane l writes LDS bytes 16l .. 16l+15 of its 1 KB, i.e. chunk position l % 16 of
-  // key row 8w + 4i + l/16, so it fetches the chunk the swizzle puts there.
+  // K/V tiles go from the pool straight into LDS (no registers in between). Only the
+  // first kLoaders wavefronts load (they get issue priority on their SIMDs and so have
+  // slack before each barrier); loader w loads keys 16w .. 16w+15 of a tile:
+  // instruction i covers keys 16w + 4i + l/16, and lane l writes LDS bytes 16l .. 16l+15
+  // of its 1 KB, i.e. chunk position l % 16 of key row 16w + 4i + l/16, so it fetches
+  // the chunk the swizzle puts there.
+  const bool loader = wave < kLoaders;
   const int64_t row_elems = (int64_t)p.num_kv_heads * kHeadDim;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_stride;
   const uint16_t* kbase = p.k_pool + (int64_t)g * kHeadDim;
@@ -277,13 +285,13 @@ void prefill_kernel(PrefillKernelArgs p) {
     return min(kt + kKeysPerWave * wave + 4 * i + (lane >> 4), key_end - 1);
   };
   // Page-table entries of a tile's keys also go straight into LDS, into a ring of
-  // kStages slots per wavefront: lane p (of the first 8) fetches the entry of the
-  // wavefront's key 4*(p%2) + p/2, so lane l later reads the entries of its two keys
-  // 4i + l/16 (i = 0, 1) as one 8-byte word at position 2*(l/16). A table index past
+  // kStages slots per loader: lane p (of the first 16) fetches the entry of the
+  // loader's key 4*(p%4) + p/4, so lane l later reads the entries of its four keys
+  // 4i + l/16 (i = 0..3) as one 16-byte word at position 4*(l/16). A table index past
   // the row reads the row's last entry.
   auto ids_dma = [&](int kt, int slot) {
-    const int p8 = lane & 7;
-    const int key = min(kt + kKeysPerWave * wave + 4 * (p8 & 1) + (p8 >> 1), key_end - 1);
+    const int p16 = lane & 15;
+    const int key = min(kt + kKeysPerWave * wave + 4 * (p16 & 3) + (p16 >> 2), key_end - 1);
     const int idx = min(page_index(key, p.pg), p.pg.table_width - 1);
     global_to_lds_b32(pt_row + idx, &ids_lds[slot][wave][0]);
   };
@@ -291,17 +299,17 @@ void prefill_kernel(PrefillKernelArgs p) {
   // ring slot `slot`. A page id outside the pool reads slot 0 (that request's result
   // is then unspecified); every access stays in bounds.
   auto dma_tile = [&](int kt, int stage, int slot) {
-    const i32x2 page = *(const i32x2*)&ids_lds[slot][wave][2 * (lane >> 4)];
+    const i32x4 page = *(const i32x4*)&ids_lds[slot][wave][4 * (lane >> 4)];
     uint16_t* kd = k_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
     uint16_t* vd = v_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int key = dma_key(kt, i);
       const int off = key - page_index(key, p.pg) * p.pg.page_size;
       const int32_t slot_i =
           (uint32_t)page[i] < (uint64_t)p.pg.num_pages ? page[i] * p.pg.page_size + off : 0;
       const int64_t row = (int64_t)slot_i * row_elems;
-      const int rr = (kKeysPerWave * wave + 4 * i + (lane >> 4)) & 15;  // key row mod 16
+      const int rr = (4 * i + (lane >> 4)) & 15;  // key row mod 16 (16w is a multiple of 16)
       global_to_lds(kbase + row + 8 * ((lane & 15) ^ rr), kd + 4 * i * kHeadDim);
       global_to_lds(vbase + row + 8 * ((lane & 15) ^ (2 * (rr & 7))), vd + 4 * i * kHeadDim);
     }
@@ -332,15 +340,16 @@ void prefill_kernel(PrefillKernelArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t4][i] = 0.f;
 
-  // Prologue: page-table entries of tiles 0..4 and the K/V of tiles 0..2 loaded.
+  // Prologue (loaders): page-table entries of tiles 0..4 and the K/V of tiles 0..2.
+  if (loader) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t) ids_dma(t * kKeysPerTile, t);
-  wait_vmcnt<0>();
+    for (int t = 0; t < 4; ++t) ids_dma(t * kKeysPerTile, t);
+    wait_vmcnt<0>();
 #pragma unroll
-  for (int t = 0; t < 3; ++t) dma_tile(t * kKeysPerTile, t, t);
-  ids_dma(3 * kKeysPerTile, 3);
-  ids_dma(4 * kKeysPerTile, 0);
-  wait_vmcnt<0>();
+    for (int t = 0; t < 3; ++t) dma_tile(t * kKeysPerTile, t, t);
+    ids_dma(4 * kKeysPerTile, 0);  // ring slot 0: tile 0's entries were read above
+    wait_vmcnt<0>();
+  }
   lds_barrier();
 
   f32x16 s[2];  // S^T of the current tile: two 32-key blocks
@@ -435,20 +444,26 @@ void prefill_kernel(PrefillKernelArgs p) {
     }
     sched_group(kSchedMfma, 4);
 
-    // Tile t+1 and the page-table entries of tile t+3 have landed: issued after them
-    // are the 4 loads of tile t+2 and the entries of tile t+4 (one load), each only if
-    // that tile exists. The barrier also shows every wavefront is done with tile t-1,
-    // whose stage the loads of tile t+3 reuse.
-    if (t + 4 < n_tiles)
-      wait_vmcnt<5>();
-    else if (t + 2 < n_tiles)
-      wait_vmcnt<4>();
-    else
-      wait_vmcnt<0>();
+    if (loader) {
+      // Tile t+3 into the stage tile t-1 used (every wavefront finished tile t-1 before
+      // the last barrier), then the page-table entries of tile t+5 (its ring slot held
+      // tile t+1's, read last iteration). Issued before this iteration's barrier, while
+      // the other wavefront of the SIMD still computes.
+      if (t + 3 < n_tiles)
+        dma_tile(kt + 3 * kKeysPerTile, (t + 3) & (kStages - 1), (t + 3) & (kStages - 1));
+      if (t + 5 < n_tiles) ids_dma(kt + 5 * kKeysPerTile, (t + 5) & (kStages - 1));
+      // Before the barrier: tile t+1 (issued two iterations ago) and the entries of tile
+      // t+4 (last iteration, after tile t+2) have landed. Issued after those entries:
+      // this iteration's 8 loads of tile t+3 and one load of entries, each only if that
+      // tile exists.
+      if (t + 5 < n_tiles)
+        wait_vmcnt<9>();
+      else if (t + 3 < n_tiles)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+    }
     lds_barrier();
-    if (t + 3 < n_tiles)
-      dma_tile(kt + 3 * kKeysPerTile, (t + 3) & (kStages - 1), (t + 3) & (kStages - 1));
-    if (t + 5 < n_tiles) ids_dma(kt + 5 * kKeysPerTile, (t + 5) & (kStages - 1));
   }
 
   if (!row_ok) return;
