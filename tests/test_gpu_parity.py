@@ -248,3 +248,72 @@ def test_decode_equals_prefill_extend_one():
     pf = host_u16(gpu_part(step, as_prefill))
     torch.cuda.synchronize()
     assert_close(d, oracle.bf16_bits_to_f64(pf), "decode vs prefill")
+
+
+@pytest.mark.parametrize("tiles", list(range(1, 10)))
+@pytest.mark.parametrize("batch", [1, 2])
+def test_prefill_block_tile_counts(tiles, batch):
+    """Blocks with exactly 1..9 key tiles of 64: the load pipeline's prologue and the
+    wait counts of its last iterations (tiles past the end are never loaded); batch 2
+    also runs the dispatch-order plan."""
+    # G = 8: 16 tokens are 128 rows, one block; keys 0 .. prefix + 15
+    prefix = 64 * (tiles - 1) + 1
+    pre, ext = [prefix] * batch, [16] * batch
+    if batch == 2:
+        pre[1], ext[1] = max(0, prefix - 40), 9   # a second, shorter request
+    step = W.build_step("tiles", 16, 2, 1, 4 * (prefix + 64) * batch,
+                        [("prefill", pre, ext)], seed=300 + tiles, device="cuda")
+    run_prefill_case(step, f"tiles={tiles} batch={batch}")
+
+
+def test_step_graph_replay_matches_eager():
+    """store + decode + prefill captured once in a HIP graph and replayed three times,
+    with eager work and synchronisation between replays: every replay reproduces the
+    eager outputs bit for bit (the calls allocate nothing and never synchronise)."""
+    import paged_kv_attention_25_amd as pka
+    step = W.build_step("graph", 16, 2, 16, 4096,
+                        [W.decode_spec([300, 1500, 40, 2048]), ("prefill", [100, 0], [70, 33])],
+                        seed=77, device="cuda", fill="zero")
+    dec, pre = step.parts
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    out_loc = i32(step.out_loc)
+    dpt, dseq = i32(dec.page_table), i32(dec.seq_lens)
+    ppt, pseq = i32(pre.page_table), i32(pre.seq_lens)
+    ppre, pext, pcu = i32(pre.prefix_lens), i32(pre.extend_lens), i32(pre.cu_extend)
+    geom = (step.num_q_heads, step.num_kv_heads, 128, step.page_size, step.num_pages)
+    dws = torch.zeros(max(1, pka.decode_workspace_bytes(*geom, dec.batch, dec.max_seq_len)),
+                      dtype=torch.uint8, device="cuda")
+    pws = torch.zeros(max(1, pka.prefill_workspace_bytes(*geom, pre.batch, pre.num_tokens,
+                                                         pre.max_extend)),
+                      dtype=torch.uint8, device="cuda")
+    dout, pout = torch.empty_like(dec.q), torch.empty_like(pre.q)
+
+    def run():
+        pka.store_kv(step.k_new, step.v_new, out_loc, step.k_pool, step.v_pool, step.page_size)
+        pka.paged_attn_decode(dec.q, step.k_pool, step.v_pool, dpt, dseq, dec.max_seq_len,
+                              step.page_size, step.scale, out=dout, workspace=dws)
+        pka.paged_attn_prefill(pre.q, step.k_pool, step.v_pool, ppt, pseq, ppre, pext, pcu,
+                               pre.max_extend, pre.max_seq_len, step.page_size, step.scale,
+                               out=pout, workspace=pws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()                      # eager reference (also warms the library's caches)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref_d, ref_p = host_u16(dout).copy(), host_u16(pout).copy()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    announce("graph replay")
+    for r in range(3):
+        dout.fill_(0)
+        pout.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(dout), ref_d), f"decode differs on replay {r}"
+        assert np.array_equal(host_u16(pout), ref_p), f"prefill differs on replay {r}"
+        run()                      # eager work between replays
+        torch.cuda.synchronize()
