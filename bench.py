@@ -157,6 +157,42 @@ def time_step(runner, steps, warmup, flush, cold=True):
     return seg, float(seg.sum()), wall
 
 
+def graph_step_us(runner, steps, flush):
+    """The whole step (store + every attention part) captured once as a HIP graph and
+    replayed: median µs per replay, caches flushed before each (launch overhead of the
+    separate calls is what the graph removes)."""
+    import torch
+    nparts = len(runner.step.parts)
+
+    def step():
+        runner.store()
+        for i in range(nparts):
+            runner.attend(i)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts))
+
+
 def cpu_baseline(step, min_seconds=10.0):
     """The oracle timed on the host (one BLAS thread) over the whole decode batch,
     repeated until at least `min_seconds` have passed."""
@@ -372,6 +408,8 @@ def main():
                     rec["prefill_TFLOPs"] = round(tf, 1)
                     rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
                     rec["prefill_flops"] = prefill_flops(p, st)
+            if name == "tiny_decode":
+                rec["graph_step_us"] = round(graph_step_us(r, args.steps, flush), 2)
             log(f"{name}: {rec}")
             parts[name] = rec
             del r, st
