@@ -125,6 +125,9 @@ class Runner:
                                         s.page_size, s.scale, out=m["out"], workspace=m["ws"])
 
 
+PART_WARMUP = 20  # warmup steps of the workloads reported under "parts"
+
+
 def time_step(runner, steps, warmup, flush, cold=True):
     """Run warmup steps, then `steps` timed steps. Each timed step records HIP events
     between its calls (store, then each attention part) on the current stream; a cache
@@ -392,7 +395,8 @@ def main():
             st = W.WORKLOADS[name](device="cuda", fill="zero")
             r = Runner(st)
             torch.cuda.synchronize()
-            seg, tot, _ = time_step(r, args.steps, args.warmup, flush)
+            # the clock under sustained MFMA load settles over some tens of steps
+            seg, tot, _ = time_step(r, args.steps, max(args.warmup, PART_WARMUP), flush)
             rec = {"step_us": round(tot * 1e3, 2), "store_us": round(seg[0] * 1e3, 2),
                    "store_GBs": round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1)}
             for i, p in enumerate(st.parts):

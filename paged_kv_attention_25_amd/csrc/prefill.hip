@@ -16,6 +16,11 @@
 // tiles earlier, so every global access of the loop is one in-order stream per loader
 // with exact waits.
 //
+// Dispatch order. Work items are (request, 256-row q tile); with several requests a
+// one-workgroup plan kernel first counting-sorts them by their number of key tiles,
+// heaviest first, and the blocks take their items in that order (a single request's
+// items already come in that order).
+//
 // LDS layout: K and V tiles are row-major (one 256-byte row per key) with the 16-byte
 // chunks of row r XOR-swizzled, by r % 16 for K and by 2*(r % 8) for V, so that the K
 // operand reads (16 bytes per lane) and the transposing V reads (8 bytes per lane)
@@ -31,9 +36,12 @@
 //    the scores lane l already holds, so P^T needs no data movement; the transposing
 //    reads fetch V rows in that order.
 // Softmax runs in the log2 domain with the scale folded into one FMA per score. The
-// running max is only raised (and the output rescaled) when it grows by more than
-// 2^8, so most tiles skip the rescale; probabilities stay below 2^8 in between.
-// Causal masking only on tiles that cross a wavefront's diagonal.
+// running max comes from the first tile; later tiles exponentiate against it without
+// computing their own maxima, and only a tile whose exponentials grow large (a lane's
+// sum of 32 past 2^32) takes its row maxima, raises the max, rescales and redoes them.
+// Probabilities therefore stay below 2^32 (bf16 and fp32 hold such values with the
+// same relative precision as values in [0, 1]). Causal masking only on tiles that
+// cross a wavefront's diagonal.
 #include "pka_device.h"
 #include "pka_kernels.h"
 
@@ -50,7 +58,7 @@ constexpr int kLoaders = kWaves / 2;                   // wavefronts that load t
 constexpr int kKeysPerWave = kKeysPerTile / kLoaders;  // keys of a tile each loader loads
 constexpr int kTileElems = kKeysPerTile * kHeadDim;   // one K or V tile: 16 KB
 constexpr int kStages = 4;  // power of two
-constexpr float kRescaleLog2 = 8.f;  // raise the running max past 2^8 growth
+constexpr float kRedoSum = 0x1p32f;  // exponential sum that makes a tile raise the max
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -390,37 +398,47 @@ void prefill_kernel(PrefillKernelArgs p) {
         for (int i = 0; i < 16; ++i)
           if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) s[kb2][i] = kNegInf;
     }
-    float mx = kNegInf;
+    // Exponentials against the running max as it stands. Only the first tile, or a
+    // tile where some lane's sum of 32 exponentials passes 2^32 (a row max above the
+    // running one by more than ~27 in log2 units), computes the tile's row maxima,
+    // raises the running max, rescales and redoes them; every other tile skips the max.
+    auto exps = [&](float neg_m) {
+      float ps = 0.f;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int u = 0; u < 4; ++u) {
+        float pr[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-    mx = max_across_halves(mx);
-    // Raw-score max; the scale is applied inside the exponent. Rescale only when
-    // some row's max grew by more than 2^kRescaleLog2 (or has no value yet).
-    const bool grow = (mx - m) * p.scale_log2 > kRescaleLog2;
-    if (__any(grow)) {
+        for (int j = 0; j < 8; ++j) {
+          pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
+          ps += pr[j];
+        }
+        pb[u][0] = pack_bf16x2(pr[0], pr[1]);
+        pb[u][1] = pack_bf16x2(pr[2], pr[3]);
+        pb[u][2] = pack_bf16x2(pr[4], pr[5]);
+        pb[u][3] = pack_bf16x2(pr[6], pr[7]);
+      }
+      return ps;
+    };
+    float ps = 0.f;
+    bool redo = t == 0;
+    if (!redo) {
+      ps = exps(-m * p.scale_log2);
+      redo = __any(ps > kRedoSum);
+    }
+    if (redo) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+      mx = max_across_halves(mx);
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
       lsum *= alpha;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) o[t4] = o[t4] * alpha;
       m = m_new;
-    }
-    const float neg_m = -m * p.scale_log2;
-    float ps = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float pr[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
-        ps += pr[j];
-      }
-      pb[u][0] = pack_bf16x2(pr[0], pr[1]);
-      pb[u][1] = pack_bf16x2(pr[2], pr[3]);
-      pb[u][2] = pack_bf16x2(pr[4], pr[5]);
-      pb[u][3] = pack_bf16x2(pr[6], pr[7]);
+      ps = exps(-m * p.scale_log2);
     }
     lsum += ps;
     // O^T += V^T P^T: d block t4, 16-key chunk u; the V^T operands are read 4 MFMAs

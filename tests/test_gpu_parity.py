@@ -188,6 +188,7 @@ def run_prefill_case(step, what, part_idx=0, windows=None):
     (16, 2, 1, [1024, 0], [300, 77]),                    # G=8
     (16, 1, 3, [7, 100], [45, 130]),                     # G=16, P=3
     (40, 8, 64, [4096, 0, 130], [33, 257, 64]),          # 14B heads, P=64
+    (16, 2, 128, [200, 0], [100, 300]),                  # pages longer than a key tile
 ])
 def test_prefill_edge_shapes(hq, hkv, page_size, prefix, extend):
     seq = np.add(prefix, extend)
@@ -248,6 +249,39 @@ def test_decode_equals_prefill_extend_one():
     pf = host_u16(gpu_part(step, as_prefill))
     torch.cuda.synchronize()
     assert_close(d, oracle.bf16_bits_to_f64(pf), "decode vs prefill")
+
+
+def scale_keys_by_position(step, part, every=64):
+    """Multiply K of logical key j of every request of `part` by 2^(j // every) (exact in
+    bf16 at these magnitudes), in the pool for prefix keys and in k_new for new ones."""
+    P = step.page_size
+    slots, slot_f, rows, row_f = [], [], [], []
+    for b in range(part.batch):
+        p, e = int(part.prefix_lens[b]), int(part.extend_lens[b])
+        for j in range(p + e):
+            f = float(2 ** (j // every))
+            if j < p:
+                slots.append(int(part.page_table[b, j // P]) * P + j % P)
+                slot_f.append(f)
+            else:
+                rows.append(part.row_offset + int(part.cu_extend[b]) + j - p)
+                row_f.append(f)
+    for t, idx, f in ((step.k_pool, slots, slot_f), (step.k_new, rows, row_f)):
+        if not idx:
+            continue
+        v = t.view(torch.bfloat16)
+        i = torch.tensor(idx, device=v.device)
+        v[i] = (v[i].float() * torch.tensor(f, device=v.device)[:, None, None]).to(torch.bfloat16)
+
+
+def test_prefill_scores_growing_with_position():
+    """Keys scaled by 2^(j // 64): from tile 3 on, row maxima exceed the running max by
+    more than 27 in log2 units, so those tiles raise the max, rescale the output and
+    redo their exponentials; the tiles before keep the max of the first tile."""
+    step = W.build_step("growing", 16, 2, 1, 2048, [("prefill", [300, 0], [70, 360])],
+                        seed=43, device="cuda")
+    scale_keys_by_position(step, step.parts[0])
+    run_prefill_case(step, "keys growing 2x per 64 positions")
 
 
 @pytest.mark.parametrize("tiles", list(range(1, 10)))
