@@ -117,14 +117,16 @@ int pka_store_kv(const pka_geom* geom, const void* k_new, const void* v_new,
  *   q             [batch, Hq, D] bf16 (device)
  *   page_table    [batch, page_table_stride] int32 page ids (device)
  *   seq_lens      [batch] int32, 1 <= L_b <= max_seq_len (device)
- *   max_seq_len   host-known upper bound of seq_lens; sets the split plan
+ *   max_seq_len   host-known upper bound of seq_lens; sets the number of wavefronts
+ *                 that share the keys (keys past it are not attended)
  *   scale         softmax scale (usually 1/sqrt(D))
  *   out           [batch, Hq, D] bf16 (device)
  *   workspace     device scratch of at least
  *                 pka_decode_workspace_bytes(geom, batch, max_seq_len) bytes (may be
  *                 NULL when that size is 0). Contents on entry are ignored. Calls
  *                 that run concurrently must not share a workspace.
- * Supported: D == 128, Hq/Hkv <= 16, batch <= 4096 (else PKA_E_UNSUPPORTED).
+ * Supported: D == 128, Hq/Hkv <= 16, batch <= 4096 and
+ * batch * Hkv * ceil(max_seq_len / 64) < 2^31 (else PKA_E_UNSUPPORTED).
  * batch == 0 is a no-op.
  */
 int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,

@@ -71,7 +71,7 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
   if (!geom || !geom_ok(geom) || batch < 0 || max_seq_len < 0) return 0;
   const int32_t group = geom->num_q_heads / geom->num_kv_heads;
   const pka::DecodePlan plan = pka::plan_decode(batch, geom->num_kv_heads, group, max_seq_len);
-  return pka::decode_workspace_bytes(batch, geom->num_q_heads, plan);
+  return pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
 }
 
 int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
@@ -86,12 +86,14 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
   if (batch == 0) return PKA_OK;
   if (max_seq_len < 1) return PKA_E_SHAPE;
   const int32_t group = geom->num_q_heads / geom->num_kv_heads;
-  if (!pka::decode_supported(batch, group)) return PKA_E_UNSUPPORTED;
+  if (!pka::decode_supported(batch, geom->num_kv_heads, group, max_seq_len))
+    return PKA_E_UNSUPPORTED;
   const int64_t pages_needed = ((int64_t)max_seq_len + geom->page_size - 1) / geom->page_size;
   if (page_table_stride < pages_needed) return PKA_E_SHAPE;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return PKA_E_NULLPTR;
   const pka::DecodePlan plan = pka::plan_decode(batch, geom->num_kv_heads, group, max_seq_len);
-  const size_t need = pka::decode_workspace_bytes(batch, geom->num_q_heads, plan);
+  const size_t need =
+      pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKA_E_WORKSPACE;
   pka::DecodeArgs a;
   a.q = q;
@@ -107,6 +109,7 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
   a.batch = batch;
   a.num_q_heads = geom->num_q_heads;
   a.num_kv_heads = geom->num_kv_heads;
+  a.max_seq_len = max_seq_len;
   a.scale = scale;
   return launch_status(pka::launch_decode(a, plan, as_stream(stream)));
 }

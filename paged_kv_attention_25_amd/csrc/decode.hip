@@ -1,23 +1,27 @@
-// Paged GQA decode for gfx950: persistent wavefronts over a dense list of key
-// chunks, then a merge pass for requests split over several chunks.
+// Paged GQA decode for gfx950: persistent wavefronts over equal shares of the batch's
+// key blocks, then a merge pass for the (request, kv head) pairs split between them.
 //
 // Batched decode reads every request's keys from the paged pool through its page
 // table ("miniSGLang intro blog", section 1.3; "Mini-SGLang deployment guide",
 // sections 6.2 and 6.3, where decode has its own kernel).
 //
-// Work decomposition. A request of L_b keys is cut into S_b = ceil(L_b / chunk)
-// chunks; a work unit is (request b, kv head g, chunk s). Each workgroup first
-// builds, in LDS, the prefix sums of S_b over the batch (and a copy of seq_lens),
-// so units are numbered densely (no empty units) with the kv head fastest. Every
-// wavefront is an independent worker over a fixed share of the units (wavefront w
-// of W takes units w, w + W, w + 2W, ...): it streams a unit's 64-key blocks,
-// writes the unit's output (or partial output) and moves on. Nothing synchronises
-// the wavefronts, and moving to the next unit reads only LDS, so a unit boundary
-// costs no memory round trip.
+// Work decomposition. Request b's keys form nb_b = ceil(L_b / 64) blocks of 64, the
+// same for each of its kv heads. The blocks of all (request, kv head) pairs are laid
+// end to end, pairs in (request, kv head) order, and wavefront w of W takes the
+// contiguous range [w*NB/W, (w+1)*NB/W) of the NB blocks (W at most NB, so no range
+// is empty), so every wavefront streams the same number of blocks (+-1). Each workgroup first builds, in LDS, the prefix
+// sums of nb_b over the batch (and a copy of seq_lens) to map a block index to its
+// (request, kv head, block). The part of one pair inside a wavefront's range is a
+// segment: a segment that is the whole pair is written to `out` directly (bf16);
+// otherwise it is a split of its pair, and its normalised partial output (f32) and
+// log2-sum-exp go to the workspace slot 2w (the wavefront's first segment) or 2w+1
+// (its last), and the merge kernel combines the splits of that pair:
+//   LSE = log2 sum_s 2^lse_s,  out = sum_s 2^(lse_s - LSE) * o_s.
+// Nothing synchronises the wavefronts, and moving to the next segment reads only LDS.
 //
 // Streaming. A wavefront holds one 64-key block (32 KB of K/V at 256-byte head
 // rows) in registers. After computing a block it issues the loads of the next block
-// - possibly in the next unit - then moves its cursor (LDS only) and issues the
+// - possibly in the next segment - then moves its cursor (LDS only) and issues the
 // page-table entries of the block after that (one entry per lane covers 64 keys).
 // Page-table entries are consumed only after the next compute, so waiting for them
 // never drains K/V loads issued after them (vmcnt counts vector memory operations
@@ -39,13 +43,9 @@
 //    in-register 8x8 transpose of bf16 pairs forms the operands.
 // Softmax is online in the log2 domain (scale*log2(e) folded into one multiply).
 //
-// A request that fits in one chunk is written to `out` directly (bf16). Otherwise
-// each chunk writes its normalised partial output (f32) and log2-sum-exp to the
-// workspace, and the merge kernel combines them:
-//   LSE = log2 sum_s 2^lse_s,  out = sum_s 2^(lse_s - LSE) * o_s.
-//
-// Workspace layout (only when some request can span several chunks): partial
-// outputs [B, Hq, S, D] f32, then their log2-sum-exps [B, Hq, S] f32.
+// Workspace layout (only when a pair can have more than one block): partial outputs
+// [2W, G, D] f32, their log2-sum-exps [2W, G] f32, then the block prefix sums over
+// the batch [B + 1] int32 (written by workgroup 0 for the merge kernel).
 #include "pka_device.h"
 #include "pka_kernels.h"
 
@@ -57,7 +57,7 @@ constexpr int kBlock = 64;        // keys per wavefront block
 constexpr int kWaves = 4;         // wavefronts per workgroup (sharing the LDS tables)
 constexpr int kMaxBatchLds = 4096;
 constexpr int kMaxGroup = 16;
-constexpr int kPlanWaves = 2048;  // resident wavefronts assumed by the chunk plan
+constexpr int kMaxDecodeWaves = 2048;  // resident wavefronts: 256 CUs x 4 SIMDs x 2
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct DecodeKernelArgs {
@@ -67,22 +67,23 @@ struct DecodeKernelArgs {
   const int32_t* __restrict__ page_table;
   const int32_t* __restrict__ seq_lens;
   uint16_t* __restrict__ out;
-  float* __restrict__ part_o;      // [B, Hq, S, D]
-  float* __restrict__ part_lse;    // [B, Hq, S]
+  float* __restrict__ part_o;        // [2W, G, D]
+  float* __restrict__ part_lse;      // [2W, G]
+  int32_t* __restrict__ req_blocks;  // [B + 1] block prefix sums (for the merge), or null
   PageGeom pg;
   int32_t pt_stride;
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t chunk;
-  int32_t num_splits;
+  int32_t max_seq_len;  // keys past it are not attended
+  int32_t waves;        // W: wavefronts sharing the blocks
   float scale_log2;
 };
 
 struct Lds {
-  int32_t prefix[kMaxBatchLds + 1];  // prefix sums of chunks per request
-  int32_t seq_len[kMaxBatchLds];     // copy of seq_lens
+  int32_t prefix[kMaxBatchLds + 1];  // prefix sums of blocks per request
+  int32_t seq_len[kMaxBatchLds];     // seq_lens, clamped to max_seq_len
   int32_t wave_tot[kWaves];
 };
 
@@ -93,17 +94,13 @@ struct Block {
   u32x4 v[2][8];   // [32-key half h][j]: key 32h + {4grp+j | 16+4grp+(j-4)}, d = 8n .. +8
 };
 
-struct Unit {
-  int32_t id;  // -1 = none
-  int32_t b, g, s, start, end, L;
-};
-
 // One block of a wavefront's stream.
 struct Desc {
   int32_t valid;
-  int32_t b, g, s;
-  int32_t k0, end, L;
-  int32_t last;  // last block of its unit
+  int32_t b, g;
+  int32_t k0, end, L;  // block start key, end of its segment's keys, request length
+  int32_t last;        // last block of its segment
+  int32_t slot;        // partial-output slot of its segment, or -1: written directly
 };
 
 struct SoftmaxState {
@@ -114,54 +111,67 @@ struct SoftmaxState {
 
 __device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ __forceinline__ Unit unit_info(int32_t u, int32_t total, const DecodeKernelArgs& p,
-                                          const Lds& lds) {
-  Unit un;
-  un.id = -1;
-  un.b = un.g = un.s = un.start = un.end = un.L = 0;
-  if (u >= total) return un;
-  const int32_t pair = u / p.num_kv_heads;
-  un.id = u;
-  un.g = u - pair * p.num_kv_heads;
-  // largest b with prefix[b] <= pair (requests with no chunks have empty ranges)
-  int32_t lo = 0, hi = p.batch;  // prefix[lo] <= pair < prefix[hi]
-  while (hi - lo > 1) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (uniform(lds.prefix[mid]) <= pair) lo = mid; else hi = mid;
-  }
-  un.b = lo;
-  un.s = pair - uniform(lds.prefix[lo]);
-  un.L = uniform(lds.seq_len[lo]);
-  un.start = un.s * p.chunk;
-  un.end = min(un.start + p.chunk, un.L);
-  return un;
+__device__ __forceinline__ int32_t blocks_of(int32_t L) { return L > 0 ? (L + kBlock - 1) / kBlock : 0; }
+
+// First block of wavefront w's range (w = W gives NB).
+__device__ __forceinline__ int32_t range_start(int32_t w, int32_t nb_total, int32_t waves) {
+  return (int32_t)(((int64_t)w * nb_total) / waves);
 }
 
-// The wavefront's cursor: the unit it is in and the next block's start. Units
-// follow with a stride of `stride` (the number of wavefronts).
+// The wavefront's cursor: the next block x of its range [x, hi) and the segment x
+// lies in.
 struct Cursor {
-  Unit un;
-  int32_t k0;
-  int32_t stride;
+  int32_t x, lo, hi;
+  int32_t b, g, L;
+  int32_t seg_end;  // end of the segment in the flattened block order
+  int32_t slot;     // -1 when the segment is its whole pair
+  int32_t j;        // block index of x within its pair
 };
 
-__device__ __forceinline__ Desc cursor_next(Cursor& c, int32_t total, const DecodeKernelArgs& p,
+// Locate flattened block x (lo <= x < hi) and set up its segment.
+__device__ __forceinline__ void locate(Cursor& c, int32_t wave_id, const DecodeKernelArgs& p,
+                                       const Lds& lds) {
+  const int32_t hkv = p.num_kv_heads;
+  // largest b with hkv*prefix[b] <= x (requests without blocks have empty ranges)
+  int32_t lo = 0, hi = p.batch;  // hkv*prefix[lo] <= x < hkv*prefix[hi]
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (hkv * uniform(lds.prefix[mid]) <= c.x) lo = mid; else hi = mid;
+  }
+  c.b = lo;
+  c.L = uniform(lds.seq_len[lo]);
+  const int32_t nb = blocks_of(c.L);
+  const int32_t r = c.x - hkv * uniform(lds.prefix[lo]);
+  c.g = uniform(r / nb);  // (a vector division; the result is wavefront-uniform)
+  const int32_t pair_start = c.x - (r - c.g * nb);
+  const int32_t pair_end = pair_start + nb;
+  c.seg_end = min(pair_end, c.hi);
+  if (pair_start >= c.lo && pair_end <= c.hi)
+    c.slot = -1;
+  else
+    c.slot = 2 * wave_id + (c.x == c.lo ? 0 : 1);
+  c.j = c.x - pair_start;
+}
+
+__device__ __forceinline__ Desc cursor_next(Cursor& c, int32_t wave_id, const DecodeKernelArgs& p,
                                             const Lds& lds) {
   Desc d;
-  d.valid = c.un.id >= 0;
-  d.b = c.un.b;
-  d.g = c.un.g;
-  d.s = c.un.s;
-  d.k0 = c.k0;
-  d.end = c.un.end;
-  d.L = c.un.L;
-  d.last = c.k0 + kBlock >= c.un.end;
-  if (!d.valid) return d;
-  c.k0 += kBlock;
-  if (c.k0 >= c.un.end) {
-    c.un = unit_info(c.un.id + c.stride, total, p, lds);
-    c.k0 = c.un.start;
+  d.valid = c.x < c.hi;
+  d.b = c.b;
+  d.g = c.g;
+  d.L = c.L;
+  d.slot = c.slot;
+  if (!d.valid) {
+    d.k0 = d.end = 0;
+    d.last = 0;
+    return d;
   }
+  d.k0 = c.j * kBlock;
+  d.end = min(c.L, (c.j + (c.seg_end - c.x)) * kBlock);
+  d.last = c.x + 1 >= c.seg_end;
+  c.x += 1;
+  c.j += 1;
+  if (c.x >= c.seg_end && c.x < c.hi) locate(c, wave_id, p, lds);
   return d;
 }
 
@@ -308,16 +318,16 @@ __device__ __forceinline__ void compute_block(const Block& blk, const Desc& d, i
   }
 }
 
-// Write one unit's result: bf16 output when the request has a single chunk, else the
-// normalised partial output and its log2-sum-exp.
-__device__ __forceinline__ void finish_unit(const Desc& d, SoftmaxState& st, int n, int grp,
-                                            const DecodeKernelArgs& p) {
+// Write one segment's result: bf16 output when the segment is its whole pair, else
+// the normalised partial output and its log2-sum-exp in the segment's slot.
+__device__ __forceinline__ void finish_segment(const Desc& d, SoftmaxState& st, int n, int grp,
+                                               const DecodeKernelArgs& p) {
   float ltot = st.lsum + __shfl_xor(st.lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   const float inv = 1.f / ltot;
   if (n < p.group) {
-    const int h = d.g * p.group + n;
-    if (d.L <= p.chunk) {
+    if (d.slot < 0) {
+      const int h = d.g * p.group + n;
       uint16_t* dst = p.out + ((int64_t)d.b * p.num_q_heads + h) * kHeadDim + 32 * grp;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -329,8 +339,8 @@ __device__ __forceinline__ void finish_unit(const Desc& d, SoftmaxState& st, int
         *(u32x4*)(dst + 8 * v) = w;
       }
     } else {
-      const int64_t unit = ((int64_t)d.b * p.num_q_heads + h) * p.num_splits + d.s;
-      float* dst = p.part_o + unit * kHeadDim + 32 * grp;
+      const int64_t row = (int64_t)d.slot * p.group + n;
+      float* dst = p.part_o + row * kHeadDim + 32 * grp;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         *(f32x4*)(dst + 8 * v) =
@@ -338,7 +348,7 @@ __device__ __forceinline__ void finish_unit(const Desc& d, SoftmaxState& st, int
         *(f32x4*)(dst + 8 * v + 4) =
             f32x4{st.o[4][v] * inv, st.o[5][v] * inv, st.o[6][v] * inv, st.o[7][v] * inv};
       }
-      if (grp == 0) p.part_lse[unit] = st.m + __builtin_log2f(ltot);
+      if (grp == 0) p.part_lse[row] = st.m + __builtin_log2f(ltot);
     }
   }
   reset_state(st);
@@ -354,17 +364,17 @@ void decode_split_kernel(DecodeKernelArgs p) {
   const int n = lane & 15;   // MFMA row/column index of this lane
   const int grp = lane >> 4; // MFMA reduction group of this lane
 
-  // Prefix sums of chunks per request (blocked scan: each thread owns a run of
-  // consecutive requests) and a copy of seq_lens.
+  // Prefix sums of blocks per request (blocked scan: each thread owns a run of
+  // consecutive requests) and a copy of seq_lens clamped to max_seq_len.
   const int per = (p.batch + kWaves * 64 - 1) / (kWaves * 64);
   const int b0 = tid * per;
   int32_t run = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < p.batch) {
-      const int32_t L = p.seq_lens[b];
+      const int32_t L = min(p.seq_lens[b], p.max_seq_len);
       lds.seq_len[b] = L;
-      run += L > 0 ? min((L + p.chunk - 1) / p.chunk, p.num_splits) : 0;
+      run += blocks_of(L);
     }
   }
   int32_t incl = run;
@@ -382,36 +392,45 @@ void decode_split_kernel(DecodeKernelArgs p) {
     const int b = b0 + i;
     if (b < p.batch) {
       lds.prefix[b] = excl;
-      const int32_t L = lds.seq_len[b];
-      excl += L > 0 ? min((L + p.chunk - 1) / p.chunk, p.num_splits) : 0;
+      if (blockIdx.x == 0 && p.req_blocks) p.req_blocks[b] = excl;
+      excl += blocks_of(lds.seq_len[b]);
     }
   }
-  if (tid == kWaves * 64 - 1) lds.prefix[p.batch] = excl;
+  if (tid == kWaves * 64 - 1) {
+    lds.prefix[p.batch] = excl;
+    if (blockIdx.x == 0 && p.req_blocks) p.req_blocks[p.batch] = excl;
+  }
   __syncthreads();
-  const int32_t total = uniform(lds.prefix[p.batch]) * p.num_kv_heads;
+  const int32_t nb_total = uniform(lds.prefix[p.batch]) * p.num_kv_heads;
+
+  // No more wavefronts than blocks, so that every range is non-empty.
+  const int32_t waves = min(p.waves, nb_total);
+  const int32_t wave_id = (int32_t)blockIdx.x * kWaves + wave;
+  if (wave_id >= waves) return;
+  Cursor cur;
+  cur.lo = uniform(range_start(wave_id, nb_total, waves));
+  cur.hi = uniform(range_start(wave_id + 1, nb_total, waves));
+  cur.x = cur.lo;
+  if (cur.x >= cur.hi) return;
+  locate(cur, wave_id, p, lds);
 
   SoftmaxState st;
   reset_state(st);
-  Cursor cur;
-  cur.stride = (int32_t)gridDim.x * kWaves;
-  cur.un = unit_info((int32_t)blockIdx.x * kWaves + wave, total, p, lds);
-  cur.k0 = cur.un.start;
-
   Block blk;
-  Desc d = cursor_next(cur, total, p, lds);
-  if (d.valid) load_block(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
-  Desc dn = cursor_next(cur, total, p, lds);
+  Desc d = cursor_next(cur, wave_id, p, lds);
+  load_block(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
+  Desc dn = cursor_next(cur, wave_id, p, lds);
   RawSlot raw_n = lookup_raw(dn, lane, p);
 
   while (d.valid) {
     compute_block(blk, d, grp, p.scale_log2, st);
     // The next block's loads go out first; the cursor (LDS only), the page-table
-    // entries of the block after and this unit's stores follow.
+    // entries of the block after and this segment's stores follow.
     const int32_t slot_n = resolve(raw_n, p);
     if (dn.valid) load_block(blk, dn, slot_n, n, grp, p);
-    const Desc dnn = cursor_next(cur, total, p, lds);
+    const Desc dnn = cursor_next(cur, wave_id, p, lds);
     raw_n = lookup_raw(dnn, lane, p);
-    if (d.last) finish_unit(d, st, n, grp, p);
+    if (d.last) finish_segment(d, st, n, grp, p);
     d = dn;
     dn = dnn;
   }
@@ -428,40 +447,67 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wavefront per (request, q head): the split weights are computed once (lane s
-// holds split s), then lane l combines d = 2l, 2l+1 over the splits, 16 at a time.
+// The wavefront whose range holds flattened block x: the largest w with
+// floor(w*NB/W) <= x, i.e. ceil((x+1)*W/NB) - 1.
+__device__ __forceinline__ int32_t wave_of(int32_t x, int32_t nb_total, int32_t waves) {
+  return (int32_t)((((int64_t)x + 1) * waves + nb_total - 1) / nb_total) - 1;
+}
+
+// One wavefront per (request, q head) of a pair split between wavefronts w0 .. w1:
+// split i comes from wavefront w0 + i, in slot 2w (that wavefront's first segment)
+// except for w0 when its range began before the pair (slot 2w0 + 1). The split
+// weights are computed once (lane s holds split s), then lane l combines d = 2l,
+// 2l+1 over the splits, 16 at a time.
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ seq_lens,
+                                                          const int32_t* __restrict__ req_blocks,
                                                           uint16_t* __restrict__ out,
-                                                          int32_t num_q_heads, int32_t chunk,
-                                                          int32_t num_splits) {
+                                                          int32_t batch, int32_t num_q_heads,
+                                                          int32_t num_kv_heads, int32_t max_seq_len,
+                                                          int32_t waves) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int L = seq_lens[b];
-  if (L <= chunk) return;  // written directly by the split kernel
-  // Keys past num_splits * chunk (a length above the planned maximum) were not
-  // attended, so only the planned splits exist in the workspace.
-  const int nsplit = min((L + chunk - 1) / chunk, num_splits);
-  const int64_t unit0 = ((int64_t)b * num_q_heads + h) * num_splits;
+  const int G = num_q_heads / num_kv_heads;
+  const int g = h / G;
+  const int nq = h - g * G;
+  const int32_t nb = blocks_of(min(seq_lens[b], max_seq_len));
+  if (nb == 0) return;
+  const int32_t nb_total = req_blocks[batch] * num_kv_heads;
+  waves = min(waves, nb_total);  // as in the split kernel
+  const int32_t S = req_blocks[b] * num_kv_heads + g * nb;
+  const int32_t w0 = wave_of(S, nb_total, waves);
+  const int32_t w1 = wave_of(S + nb - 1, nb_total, waves);
+  if (w0 == w1) return;  // written directly by the split kernel
+  const int32_t first0 = range_start(w0, nb_total, waves) == S ? 0 : 1;
+  const int nsplit = w1 - w0 + 1;
+  // row of split i in part_o / part_lse
+  auto row_of = [&](int i) -> int64_t {
+    const int32_t slot = i == 0 ? 2 * w0 + first0 : 2 * (w0 + i);
+    return (int64_t)slot * G + nq;
+  };
   float mx = kNegInf;
   for (int s0 = 0; s0 < nsplit; s0 += 64)
-    mx = fmaxf(mx, s0 + lane < nsplit ? part_lse[unit0 + s0 + lane] : kNegInf);
+    mx = fmaxf(mx, s0 + lane < nsplit ? part_lse[row_of(s0 + lane)] : kNegInf);
   mx = wave_max(mx);
   float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += 64) {
-    const float w_l = s0 + lane < nsplit ? fast_exp2(part_lse[unit0 + s0 + lane] - mx) : 0.f;
+    const int my = s0 + lane;
+    const float w_l = my < nsplit ? fast_exp2(part_lse[row_of(my)] - mx) : 0.f;
+    const int64_t row_l = my < nsplit ? row_of(my) : 0;
     wsum += w_l;
     const int cnt = min(64, nsplit - s0);
-    const float* src = part_o + (unit0 + s0) * kHeadDim + 2 * lane;
     // 16 splits' loads in flight at a time: a long row's merge is a chain of
     // dependent memory latencies otherwise.
     int s = 0;
     for (; s + 16 <= cnt; s += 16) {
       float2 v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = *(const float2*)(src + (int64_t)(s + i) * kHeadDim);
+      for (int i = 0; i < 16; ++i) {
+        const int64_t r = __shfl(row_l, s + i);
+        v[i] = *(const float2*)(part_o + r * kHeadDim + 2 * lane);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float w = __shfl(w_l, s + i);
@@ -469,19 +515,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
         acc1 += w * v[i].y;
       }
     }
-    for (; s + 4 <= cnt; s += 4) {
-      float2 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = *(const float2*)(src + (int64_t)(s + i) * kHeadDim);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float w = __shfl(w_l, s + i);
-        acc0 += w * v[i].x;
-        acc1 += w * v[i].y;
-      }
-    }
     for (; s < cnt; ++s) {
-      const float2 v = *(const float2*)(src + (int64_t)s * kHeadDim);
+      const int64_t r = __shfl(row_l, s);
+      const float2 v = *(const float2*)(part_o + r * kHeadDim + 2 * lane);
       const float w = __shfl(w_l, s);
       acc0 += w * v.x;
       acc1 += w * v.y;
@@ -492,49 +528,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
 }
 
-int device_workgroups() {
-  // Resident workgroups: 2 per CU (8 wavefronts of 256 registers each).
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanWaves / kWaves;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = kPlanWaves / (2 * kWaves);
-    cached[dev] = 2 * cus;
-  }
-  return cached[dev];
-}
-
 }  // namespace
 
-bool decode_supported(int32_t batch, int32_t group) {
-  return batch <= kMaxBatchLds && group <= kMaxGroup;
+bool decode_supported(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len) {
+  const int64_t blocks = (int64_t)batch * num_kv_heads * ((max_seq_len + kBlock - 1) / kBlock);
+  return batch <= kMaxBatchLds && group <= kMaxGroup && blocks < ((int64_t)1 << 31);
 }
 
 DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len) {
-  // Largest power-of-two chunk in [max(128, 16*G), 4096] whose upper-bound unit count
-  // (every request at max_seq_len) reaches 8 units per resident wavefront, so the
-  // round-robin assignment balances well; the floor keeps a chunk's partial output
-  // (G*D floats, written and read back once) near 3% of its K/V bytes.
+  // As many wavefronts as fit resident, but no more than the most blocks the batch can
+  // have; a pair can be split only when it can have two or more blocks.
   DecodePlan plan;
-  const int64_t pairs = (int64_t)batch * num_kv_heads;
-  const int64_t msl = max_seq_len > 0 ? max_seq_len : 1;
-  int64_t floor_chunk = 16 * (int64_t)group;
-  if (floor_chunk < 2 * kBlock) floor_chunk = 2 * kBlock;
-  int64_t chunk = 4096;
-  while (chunk > floor_chunk && pairs * ((msl + chunk - 1) / chunk) < 8 * kPlanWaves) chunk >>= 1;
-  if (chunk < floor_chunk) chunk = floor_chunk;
-  plan.chunk = (int32_t)chunk;
-  plan.num_splits = (int32_t)((msl + chunk - 1) / chunk);
+  const int64_t per_pair = max_seq_len > 0 ? ((int64_t)max_seq_len + kBlock - 1) / kBlock : 0;
+  const int64_t blocks = (int64_t)batch * num_kv_heads * per_pair;
+  plan.waves = (int32_t)(blocks < kMaxDecodeWaves ? (blocks > 0 ? blocks : 1) : kMaxDecodeWaves);
+  plan.splits = per_pair > 1;
+  (void)group;
   return plan;
 }
 
-size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, const DecodePlan& plan) {
-  if (plan.num_splits <= 1) return 0;
-  const size_t units = (size_t)batch * num_q_heads * plan.num_splits;
-  return units * (kHeadDim + 1) * sizeof(float);
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              const DecodePlan& plan) {
+  if (!plan.splits) return 0;
+  const size_t rows = (size_t)2 * plan.waves * (num_q_heads / num_kv_heads);
+  return rows * (kHeadDim + 1) * sizeof(float) + ((size_t)batch + 1) * sizeof(int32_t);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
@@ -546,27 +563,27 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   k.page_table = a.page_table;
   k.seq_lens = a.seq_lens;
   k.out = (uint16_t*)a.out;
-  const size_t units = (size_t)a.batch * a.num_q_heads * plan.num_splits;
-  k.part_o = (float*)a.workspace;
-  k.part_lse = plan.num_splits > 1 ? k.part_o + units * kHeadDim : nullptr;
+  const int32_t group = a.num_q_heads / a.num_kv_heads;
+  const size_t rows = (size_t)2 * plan.waves * group;
+  k.part_o = plan.splits ? (float*)a.workspace : nullptr;
+  k.part_lse = plan.splits ? k.part_o + rows * kHeadDim : nullptr;
+  k.req_blocks = plan.splits ? (int32_t*)(k.part_lse + rows) : nullptr;
   k.pg = make_page_geom(a.page_size, a.pt_stride, a.num_pages);
   k.pt_stride = a.pt_stride;
   k.batch = a.batch;
   k.num_q_heads = a.num_q_heads;
   k.num_kv_heads = a.num_kv_heads;
-  k.group = a.num_q_heads / a.num_kv_heads;
-  k.chunk = plan.chunk;
-  k.num_splits = plan.num_splits;
+  k.group = group;
+  k.max_seq_len = a.max_seq_len;
+  k.waves = plan.waves;
   k.scale_log2 = a.scale * kLog2e;
-  const int64_t max_units = (int64_t)a.batch * a.num_kv_heads * plan.num_splits;
-  int64_t grid = device_workgroups();
-  if (grid * kWaves > max_units) grid = (max_units + kWaves - 1) / kWaves;
+  const int grid = (plan.waves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, k);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.num_splits <= 1) return err;
+  if (err != hipSuccess || !plan.splits) return err;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(a.num_q_heads, a.batch), dim3(64), 0, stream,
-                     k.part_o, k.part_lse, a.seq_lens, (uint16_t*)a.out, a.num_q_heads,
-                     plan.chunk, plan.num_splits);
+                     k.part_o, k.part_lse, a.seq_lens, k.req_blocks, (uint16_t*)a.out, a.batch,
+                     a.num_q_heads, a.num_kv_heads, a.max_seq_len, plan.waves);
   return hipGetLastError();
 }
 

@@ -21,16 +21,19 @@ struct StoreArgs {
 };
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t stream);
 
-// Split plan of the decode kernel: keys of request b are cut into chunks of
-// `chunk` tokens; chunk s of request b is one work unit.
+// Plan of the decode kernel: `waves` wavefronts share the batch's 64-key blocks
+// (equal contiguous ranges); `splits` when a (request, kv head) pair can have two or
+// more blocks and so be split between wavefronts (then a merge pass runs).
 struct DecodePlan {
-  int32_t chunk;
-  int32_t num_splits;  // ceil(max_seq_len / chunk)
+  int32_t waves;
+  bool splits;
 };
 DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len);
-// Whether the decode kernel supports this batch size and group size (q heads per kv head).
-bool decode_supported(int32_t batch, int32_t group);
-size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, const DecodePlan& plan);
+// Whether the decode kernel supports this shape: batch, group size (q heads per kv
+// head) and total block count (batch * Hkv * ceil(max_seq_len / 64) below 2^31).
+bool decode_supported(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len);
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              const DecodePlan& plan);
 
 struct DecodeArgs {
   const void* q;
@@ -46,6 +49,7 @@ struct DecodeArgs {
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t max_seq_len;  // keys past it are not attended
   float scale;
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);

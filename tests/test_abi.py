@@ -73,11 +73,15 @@ def prefill(L, g, batch=2, tokens=10, max_ext=6, max_seq=20, stride=20, q=FAKE, 
 
 def test_workspace_sizes(L):
     g = geom()
-    # one chunk covers everything: no split, no workspace
+    # one 64-key block per (request, kv head): never split, no workspace
     assert L.pka_decode_workspace_bytes(ctypes.byref(g), 1, 64) == 0
-    # long sequences split: partial o (D floats) + lse per (request, q head, split)
-    n = L.pka_decode_workspace_bytes(ctypes.byref(g), 32, 32768)
-    assert n > 0 and n % (129 * 4) == 0
+    # otherwise 2 partial slots per wavefront (G rows of D floats + lse each) and the
+    # block prefix sums over the batch; wavefronts = min(2048, blocks the batch can have)
+    G = 2
+    assert L.pka_decode_workspace_bytes(ctypes.byref(g), 32, 32768) == \
+        2 * 2048 * G * 129 * 4 + 33 * 4
+    assert L.pka_decode_workspace_bytes(ctypes.byref(g), 4, 100) == \
+        2 * (4 * 8 * 2) * G * 129 * 4 + 5 * 4
     assert L.pka_decode_workspace_bytes(None, 4, 100) == 0
     # prefill: one int32 per (request, 256-row q tile) item when batch > 1, else 0
     assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 1, 10, 6) == 0
@@ -92,6 +96,9 @@ def test_decode_argument_errors(L):
     assert decode(L, geom(page_size=0)) == pka.PKA_E_SHAPE
     assert decode(L, geom(head_dim=64)) == pka.PKA_E_UNSUPPORTED
     assert decode(L, geom(num_q_heads=64, num_kv_heads=2)) == pka.PKA_E_UNSUPPORTED  # G > 16
+    # 4096 requests x 8 kv heads x 65536 blocks of 64 keys = 2^31 blocks
+    assert decode(L, geom(), batch=4096, max_seq=1 << 22, stride=1 << 22) == \
+        pka.PKA_E_UNSUPPORTED
     assert decode(L, geom(), batch=-1) == pka.PKA_E_SHAPE
     assert decode(L, geom(), max_seq=0) == pka.PKA_E_SHAPE
     assert decode(L, geom(), stride=100, max_seq=250) == pka.PKA_E_SHAPE  # table too narrow

@@ -126,30 +126,34 @@ def test_decode_single_key_is_v_exactly():
 
 
 def test_decode_split_count_invariance():
-    """The same batch planned with different max_seq_len hints (so different chunk
-    sizes and split counts) agrees within tolerance."""
-    step = W.build_step("splits", 16, 8, 1, 1 << 14, [W.decode_spec([3000, 4096, 777])], seed=23,
+    """Requests split at different keys agree within tolerance: three requests decoded
+    alone (992 blocks of 64 keys for 992 wavefronts, one block each, so every (request,
+    kv head) pair is merged from many splits) and inside a batch of 23 (6112 blocks for
+    2048 wavefronts, about three each, other split points), and with a max_seq_len hint
+    far above the lengths (the plan's wavefront count is capped by the actual blocks)."""
+    lens = [3000, 4096, 777] + [2000] * 20
+    step = W.build_step("splits", 16, 8, 1, 1 << 16, [W.decode_spec(lens)], seed=23,
                         device="cuda")
-    part = step.parts[0]
+    big = step.parts[0]
     hint = 200000
-    # a wider table (padded with its own pad entry) admits the larger max_seq_len hint
-    part.page_table = np.pad(part.page_table, ((0, 0), (0, hint - part.page_table.shape[1])),
-                             mode="edge")
-    import paged_kv_attention_25_amd as pka
-    ws = [pka.decode_workspace_bytes(16, 8, 128, 1, 1 << 14, 3, m) for m in (4096, hint)]
-    # the two hints give different split plans (different split counts)
-    per_split = 3 * 16 * 129 * 4      # partial o + lse per split
-    assert all(w % per_split == 0 for w in ws) and ws[0] != ws[1]
+    small = W.AttnPart(kind="decode", seq_lens=big.seq_lens[:3], prefix_lens=big.prefix_lens[:3],
+                       extend_lens=big.extend_lens[:3], cu_extend=big.cu_extend[:4],
+                       page_table=np.pad(big.page_table[:3],
+                                         ((0, 0), (0, hint - big.page_table.shape[1])),
+                                         mode="edge"),
+                       q=big.q[:3].contiguous(), row_offset=0)
     host = HostInputs(step)
     check_store(step, host, "splits")
     announce("decode split-count invariance")
-    a = host_u16(gpu_part(step, step.parts[0]))
-    b = host_u16(gpu_part(step, step.parts[0], max_seq_len=hint))
+    a = host_u16(gpu_part(step, small))
+    b = host_u16(gpu_part(step, big))[:3]
+    c = host_u16(gpu_part(step, small, max_seq_len=hint))
     torch.cuda.synchronize()
-    ref, _ = oracle_decode(step, host, 0)
-    assert_close(a, ref, "plan A")
-    assert_close(b, ref, "plan B")
-    assert_close(a, oracle.bf16_bits_to_f64(b), "plan A vs plan B")
+    ref, _ = oracle_decode(step, host, 0, requests=[0, 1, 2])
+    assert_close(a, ref, "alone")
+    assert_close(b, ref, "in a batch of 23")
+    assert_close(c, ref, "alone, large max_seq_len hint")
+    assert_close(a, oracle.bf16_bits_to_f64(b), "alone vs in the batch")
 
 
 def test_decode_gqa_constant_v():
