@@ -115,6 +115,18 @@ def test_decode_edge_shapes(hq, hkv, page_size, lens):
     run_decode_case(step, f"edge hq={hq} hkv={hkv} P={page_size} L={lens}")
 
 
+def test_decode_max_batch():
+    """The largest supported batch (4096 requests, lengths 1..200): the per-request block
+    prefix sums are built with 16 requests per thread, and most wavefront ranges hold
+    several whole pairs (written directly) besides the split ones."""
+    rng = np.random.default_rng(25)
+    lens = rng.integers(1, 201, size=4096)
+    step = W.build_step("max_batch", 16, 2, 1, int(lens.sum()) + 64, [W.decode_spec(lens)],
+                        seed=25, device="cuda")
+    run_decode_case(step, "max batch 4096, 16q/2kv, L in [1, 200]",
+                    requests=list(range(0, 4096, 37)) + [4095])
+
+
 def test_decode_single_key_is_v_exactly():
     step = W.build_step("single", 16, 8, 1, 64, [W.decode_spec([1, 1, 1])], seed=22,
                         device="cuda")
@@ -200,6 +212,18 @@ def test_prefill_edge_shapes(hq, hkv, page_size, prefix, extend):
     step = W.build_step("edge", hq, hkv, page_size, pages, [("prefill", prefix, extend)],
                         seed=31, device="cuda")
     run_prefill_case(step, f"edge hq={hq} hkv={hkv} P={page_size} p={prefix} e={extend}")
+
+
+def test_prefill_many_small_requests():
+    """600 requests of 0..12 new tokens on prefixes of 0..300: many one-block work items
+    with mixed key counts through the dispatch-order plan (empty requests included)."""
+    rng = np.random.default_rng(26)
+    prefix = rng.integers(0, 301, size=600)
+    extend = rng.integers(0, 13, size=600)
+    pages = int(sum(-(-int(L) // 16) for L in prefix + extend)) + 8
+    step = W.build_step("many_small", 16, 2, 16, pages, [("prefill", prefix, extend)], seed=26,
+                        device="cuda")
+    run_prefill_case(step, "600 small requests, P=16")
 
 
 def test_prefill_chunked_sampled():
