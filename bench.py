@@ -125,7 +125,7 @@ class Runner:
                                         s.page_size, s.scale, out=m["out"], workspace=m["ws"])
 
 
-PART_WARMUP = 20  # warmup steps of the workloads reported under "parts"
+PART_WARMUP = 60  # warmup steps of the workloads reported under "parts"
 
 
 def time_step(runner, steps, warmup, flush, cold=True):
