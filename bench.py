@@ -314,8 +314,8 @@ def main():
         write_traffic(*args.traffic_from)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "the attention path here runs on one GPU only; --gpus must "
+                          "be 1 (sharding across GPUs is a design note, not implemented)"}))
         sys.exit(2)
 
     import torch
