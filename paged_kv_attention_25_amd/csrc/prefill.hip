@@ -256,6 +256,7 @@ void prefill_kernel(PrefillKernelArgs p) {
   // The wavefront's smallest limit (rows are in token order).
   const int wrow_first = row0 + wave * kRowsPerWave;
   const int wave_lim_lo = prefix + (wrow_first < nrows ? wrow_first / G : 0);
+  const bool active = wrow_first < nrows;  // the wavefront has rows of the block
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kStages * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kStages * kTileElems];
@@ -369,99 +370,104 @@ void prefill_kernel(PrefillKernelArgs p) {
     const uint16_t* kt_lds = k_lds + stage * kTileElems;
     const uint16_t* vt_lds = v_lds + stage * kTileElems;
 
-    // S^T = K Q^T for the tile's two 32-key blocks. The K operands are read 8 MFMAs
-    // ahead of their use (the schedule below), so LDS latency stays hidden.
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4 a = *(const u32x4*)(kt_lds + 32 * kb2 * kHeadDim + k_rd[c]);
-        s[kb2] = mfma_32x32x16(a, qv[c], s[kb2]);
-      }
-    }
-    sched_group(kSchedDsRead, 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sched_group(kSchedMfma, 1);
-      sched_group(kSchedDsRead, 1);
-    }
-    sched_group(kSchedMfma, 8);
-    // Causal mask only where the tile crosses this wavefront's diagonal: register i
-    // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
-    if (kt + kKeysPerTile - 1 > wave_lim_lo) {
-      const int dl = lim - kt - 4 * hgrp;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) s[kb2][i] = kNegInf;
-    }
-    // Exponentials against the running max as it stands. Only the first tile, or a
-    // tile where some lane's sum of 32 exponentials passes 2^32 (a row max above the
-    // running one by more than ~27 in log2 units), computes the tile's row maxima,
-    // raises the running max, rescales and redoes them; every other tile skips the max.
-    auto exps = [&](float neg_m) {
-      float ps = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float pr[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
-          ps += pr[j];
+    // A wavefront whose 32 rows all lie past the block's rows (the last q tile of a
+    // request) skips the compute and only copies and waits, leaving its SIMD to the
+    // other wavefront.
+    if (active) {
+      // S^T = K Q^T for the tile's two 32-key blocks. The K operands are read 8 MFMAs
+      // ahead of their use (the schedule below), so LDS latency stays hidden.
+  #pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
+  #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 a = *(const u32x4*)(kt_lds + 32 * kb2 * kHeadDim + k_rd[c]);
+          s[kb2] = mfma_32x32x16(a, qv[c], s[kb2]);
         }
-        pb[u][0] = pack_bf16x2(pr[0], pr[1]);
-        pb[u][1] = pack_bf16x2(pr[2], pr[3]);
-        pb[u][2] = pack_bf16x2(pr[4], pr[5]);
-        pb[u][3] = pack_bf16x2(pr[6], pr[7]);
       }
-      return ps;
-    };
-    float ps = 0.f;
-    bool redo = t == 0;
-    if (!redo) {
-      ps = exps(-m * p.scale_log2);
-      redo = __any(ps > kRedoSum);
-    }
-    if (redo) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-      mx = max_across_halves(mx);
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
-      lsum *= alpha;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) o[t4] = o[t4] * alpha;
-      m = m_new;
-      ps = exps(-m * p.scale_log2);
-    }
-    lsum += ps;
-    // O^T += V^T P^T: d block t4, 16-key chunk u; the V^T operands are read 4 MFMAs
-    // ahead of their use.
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const uint16_t* src = vt_lds + 16 * u * kHeadDim + v_rd[t4];
-        const u32x2 lo = tr_read(src);
-        const u32x2 hi = tr_read(src + 8 * kHeadDim);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        o[t4] = mfma_32x32x16(a, pb[u], o[t4]);
+      sched_group(kSchedDsRead, 8);
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedDsRead, 1);
       }
-    }
-    sched_group(kSchedDsRead, 8);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      sched_group(kSchedMfma, 1);
-      sched_group(kSchedDsRead, 2);
-    }
-    sched_group(kSchedMfma, 4);
+      sched_group(kSchedMfma, 8);
+      // Causal mask only where the tile crosses this wavefront's diagonal: register i
+      // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
+      if (kt + kKeysPerTile - 1 > wave_lim_lo) {
+        const int dl = lim - kt - 4 * hgrp;
+  #pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) s[kb2][i] = kNegInf;
+      }
+      // Exponentials against the running max as it stands. Only the first tile, or a
+      // tile where some lane's sum of 32 exponentials passes 2^32 (a row max above the
+      // running one by more than ~27 in log2 units), computes the tile's row maxima,
+      // raises the running max, rescales and redoes them; every other tile skips the max.
+      auto exps = [&](float neg_m) {
+        float ps = 0.f;
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float pr[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
+            ps += pr[j];
+          }
+          pb[u][0] = pack_bf16x2(pr[0], pr[1]);
+          pb[u][1] = pack_bf16x2(pr[2], pr[3]);
+          pb[u][2] = pack_bf16x2(pr[4], pr[5]);
+          pb[u][3] = pack_bf16x2(pr[6], pr[7]);
+        }
+        return ps;
+      };
+      float ps = 0.f;
+      bool redo = t == 0;
+      if (!redo) {
+        ps = exps(-m * p.scale_log2);
+        redo = __any(ps > kRedoSum);
+      }
+      if (redo) {
+        float mx = kNegInf;
+  #pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+        mx = max_across_halves(mx);
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
+        lsum *= alpha;
+  #pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) o[t4] = o[t4] * alpha;
+        m = m_new;
+        ps = exps(-m * p.scale_log2);
+      }
+      lsum += ps;
+      // O^T += V^T P^T: d block t4, 16-key chunk u; the V^T operands are read 4 MFMAs
+      // ahead of their use.
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+  #pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const uint16_t* src = vt_lds + 16 * u * kHeadDim + v_rd[t4];
+          const u32x2 lo = tr_read(src);
+          const u32x2 hi = tr_read(src + 8 * kHeadDim);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          o[t4] = mfma_32x32x16(a, pb[u], o[t4]);
+        }
+      }
+      sched_group(kSchedDsRead, 8);
+  #pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedDsRead, 2);
+      }
+      sched_group(kSchedMfma, 4);
 
+    }
     if (loader) {
       // Tile t+3 into the stage tile t-1 used (every wavefront finished tile t-1 before
       // the last barrier), then the page-table entries of tile t+5 (its ring slot held
