@@ -376,18 +376,18 @@ void prefill_kernel(PrefillKernelArgs p) {
     if (active) {
       // S^T = K Q^T for the tile's two 32-key blocks. The K operands are read 8 MFMAs
       // ahead of their use (the schedule below), so LDS latency stays hidden.
-  #pragma unroll
+#pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; ++c) {
           const u32x4 a = *(const u32x4*)(kt_lds + 32 * kb2 * kHeadDim + k_rd[c]);
           s[kb2] = mfma_32x32x16(a, qv[c], s[kb2]);
         }
       }
       sched_group(kSchedDsRead, 8);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 8; ++i) {
         sched_group(kSchedMfma, 1);
         sched_group(kSchedDsRead, 1);
@@ -397,9 +397,9 @@ void prefill_kernel(PrefillKernelArgs p) {
       // of block kb2 holds key kt + 32*kb2 + 8*(i/4) + 4*hgrp + (i%4).
       if (kt + kKeysPerTile - 1 > wave_lim_lo) {
         const int dl = lim - kt - 4 * hgrp;
-  #pragma unroll
+#pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i)
             if (32 * kb2 + 8 * (i >> 2) + (i & 3) > dl) s[kb2][i] = kNegInf;
       }
@@ -409,10 +409,10 @@ void prefill_kernel(PrefillKernelArgs p) {
       // raises the running max, rescales and redoes them; every other tile skips the max.
       auto exps = [&](float neg_m) {
         float ps = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 4; ++u) {
           float pr[8];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 8; ++j) {
             pr[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], p.scale_log2, neg_m));
             ps += pr[j];
@@ -432,15 +432,15 @@ void prefill_kernel(PrefillKernelArgs p) {
       }
       if (redo) {
         float mx = kNegInf;
-  #pragma unroll
+#pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
         mx = max_across_halves(mx);
         const float m_new = fmaxf(m, mx);
         const float alpha = fast_exp2((m - m_new) * p.scale_log2);  // 0 when m = -inf
         lsum *= alpha;
-  #pragma unroll
+#pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) o[t4] = o[t4] * alpha;
         m = m_new;
         ps = exps(-m * p.scale_log2);
@@ -448,9 +448,9 @@ void prefill_kernel(PrefillKernelArgs p) {
       lsum += ps;
       // O^T += V^T P^T: d block t4, 16-key chunk u; the V^T operands are read 4 MFMAs
       // ahead of their use.
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < 4; ++u) {
-  #pragma unroll
+#pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           const uint16_t* src = vt_lds + 16 * u * kHeadDim + v_rd[t4];
           const u32x2 lo = tr_read(src);
@@ -460,13 +460,12 @@ void prefill_kernel(PrefillKernelArgs p) {
         }
       }
       sched_group(kSchedDsRead, 8);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 12; ++i) {
         sched_group(kSchedMfma, 1);
         sched_group(kSchedDsRead, 2);
       }
       sched_group(kSchedMfma, 4);
-
     }
     if (loader) {
       // Tile t+3 into the stage tile t-1 used (every wavefront finished tile t-1 before
