@@ -1,6 +1,7 @@
 """Benchmark of the paged KV-cache attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+    python bench.py --part WORKLOAD [--steps K] [--warmup W]   (one workload, for profiling)
 
 Prints ONE JSON line. The headline workload is the offline-style decode batch
 (Qwen3-0.6B heads 16q/8kv, d=128, bf16, batch 256, context lengths uniform in
@@ -297,6 +298,53 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+def calibration_copy(flush):
+    """Two plain device copies of COPY_BYTES: the reference for the traffic counters."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        flush()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+PART_NAMES = ("chunked_prefill", "tp4_mixed", "long_decode", "tiny_decode")
+
+
+def time_part(name, steps, warmup, flush, log):
+    """Time one of the non-headline workloads; per-segment medians in its record."""
+    import torch
+    from paged_kv_attention_25_amd import workloads as W
+    log(f"{name}: generating inputs")
+    st = W.WORKLOADS[name](device="cuda", fill="zero")
+    r = Runner(st)
+    torch.cuda.synchronize()
+    seg, tot, _ = time_step(r, steps, warmup, flush)
+    rec = {"step_us": round(tot * 1e3, 2), "store_us": round(seg[0] * 1e3, 2),
+           "store_GBs": round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1)}
+    for i, p in enumerate(st.parts):
+        us = seg[i + 1] * 1e3
+        if p.kind == "decode":
+            gbs = decode_bytes(p, st) / (us * 1e-6) / 1e9
+            rec["decode_us"] = round(us, 2)
+            rec["decode_GBs"] = round(gbs, 1)
+            rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        else:
+            tf = prefill_flops(p, st) / (us * 1e-6) / 1e12
+            rec["prefill_us"] = round(us, 2)
+            rec["prefill_TFLOPs"] = round(tf, 1)
+            rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+            rec["prefill_flops"] = prefill_flops(p, st)
+    if name == "tiny_decode":
+        rec["graph_step_us"] = round(graph_step_us(r, steps, flush), 2)
+    log(f"{name}: {rec}")
+    del r, st
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +357,9 @@ def main():
                     help="also run two 512 MiB device copies (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the decode_b256 traffic record from two counter runs, then exit")
+    ap.add_argument("--part", choices=PART_NAMES,
+                    help="time only this workload (its warmup is --warmup), print its record, "
+                         "exit (for profiling one workload)")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
@@ -335,6 +386,14 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.part:
+        if args.calibration_copy:
+            calibration_copy(flush)
+        print(json.dumps({"part": args.part,
+                          **time_part(args.part, args.steps, args.warmup, flush, log)}),
+              flush=True)
+        return
 
     # --- headline: decode_b256 ------------------------------------------------------
     log("decode_b256: generating inputs")
@@ -369,13 +428,7 @@ def main():
         "roofline": roofline,
     }
     if args.calibration_copy:
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            flush()
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(flush)
     if args.hot:
         seg_h, tot_h, _ = time_step(run, args.steps, 0, flush, cold=False)
         result["config"]["hot_cache_decode_GBs"] = round(dec_bytes / (seg_h[1] * 1e-3) / 1e9, 1)
@@ -390,34 +443,8 @@ def main():
 
     parts = {}
     if not args.quick:
-        for name in ("chunked_prefill", "tp4_mixed", "long_decode", "tiny_decode"):
-            log(f"{name}: generating inputs")
-            st = W.WORKLOADS[name](device="cuda", fill="zero")
-            r = Runner(st)
-            torch.cuda.synchronize()
-            # the clock under sustained MFMA load settles over some tens of steps
-            seg, tot, _ = time_step(r, args.steps, max(args.warmup, PART_WARMUP), flush)
-            rec = {"step_us": round(tot * 1e3, 2), "store_us": round(seg[0] * 1e3, 2),
-                   "store_GBs": round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1)}
-            for i, p in enumerate(st.parts):
-                us = seg[i + 1] * 1e3
-                if p.kind == "decode":
-                    gbs = decode_bytes(p, st) / (us * 1e-6) / 1e9
-                    rec["decode_us"] = round(us, 2)
-                    rec["decode_GBs"] = round(gbs, 1)
-                    rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
-                else:
-                    tf = prefill_flops(p, st) / (us * 1e-6) / 1e12
-                    rec["prefill_us"] = round(us, 2)
-                    rec["prefill_TFLOPs"] = round(tf, 1)
-                    rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-                    rec["prefill_flops"] = prefill_flops(p, st)
-            if name == "tiny_decode":
-                rec["graph_step_us"] = round(graph_step_us(r, args.steps, flush), 2)
-            log(f"{name}: {rec}")
-            parts[name] = rec
-            del r, st
-            torch.cuda.empty_cache()
+        for name in PART_NAMES:
+            parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log)
         cp = parts["chunked_prefill"]
         result["prefill"] = {"workload": "chunked_prefill: Qwen3-14B heads 40q/8kv, 32 requests, "
                                          "prefixes U[0,4096], 8192 new tokens, page_size 16",
