@@ -453,22 +453,24 @@ __device__ __forceinline__ int32_t wave_of(int32_t x, int32_t nb_total, int32_t 
   return (int32_t)((((int64_t)x + 1) * waves + nb_total - 1) / nb_total) - 1;
 }
 
-// One wavefront per (request, q head) of a pair split between wavefronts w0 .. w1:
-// split i comes from wavefront w0 + i, in slot 2w (that wavefront's first segment)
-// except for w0 when its range began before the pair (slot 2w0 + 1). The split
-// weights are computed once (lane s holds split s), then lane l combines d = 2l,
-// 2l+1 over the splits, 16 at a time.
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse,
-                                                          const int32_t* __restrict__ seq_lens,
-                                                          const int32_t* __restrict__ req_blocks,
-                                                          uint16_t* __restrict__ out,
-                                                          int32_t batch, int32_t num_q_heads,
-                                                          int32_t num_kv_heads, int32_t max_seq_len,
-                                                          int32_t waves) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+// One wavefront per (request, q head) of a pair split between wavefronts w0 .. w1,
+// four per workgroup: split i comes from wavefront w0 + i, in slot 2w (that
+// wavefront's first segment) except for w0 when its range began before the pair
+// (slot 2w0 + 1). Lane l combines d = 2l, 2l+1. Up to 16 splits (the usual case) are
+// merged with one round of loads: lane s loads split s's log2-sum-exp while every lane
+// loads its part of all splits' outputs; longer rows go through a loop of 64 splits
+// at a time.
+constexpr int kMergeWaves = 4;
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ req_blocks,
+    uint16_t* __restrict__ out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t max_seq_len, int32_t waves) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (row >= (int64_t)batch * num_q_heads) return;
+  const int b = (int)(row / num_q_heads);
+  const int h = (int)(row - (int64_t)b * num_q_heads);
   const int G = num_q_heads / num_kv_heads;
   const int g = h / G;
   const int nq = h - g * G;
@@ -487,6 +489,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     const int32_t slot = i == 0 ? 2 * w0 + first0 : 2 * (w0 + i);
     return (int64_t)slot * G + nq;
   };
+  uint32_t* dst = (uint32_t*)(out + ((int64_t)b * num_q_heads + h) * kHeadDim);
+  if (nsplit <= 16) {
+    const float lse_l = lane < nsplit ? part_lse[row_of(lane)] : kNegInf;
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = i < nsplit ? *(const float2*)(part_o + row_of(i) * kHeadDim + 2 * lane)
+                        : float2{0.f, 0.f};
+    const float mx = wave_max(lse_l);
+    const float w_l = lane < nsplit ? fast_exp2(lse_l - mx) : 0.f;
+    const float inv = 1.f / wave_sum(w_l);
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float w = __shfl(w_l, i);  // 0 past nsplit
+      acc0 += w * v[i].x;
+      acc1 += w * v[i].y;
+    }
+    dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
+    return;
+  }
   float mx = kNegInf;
   for (int s0 = 0; s0 < nsplit; s0 += 64)
     mx = fmaxf(mx, s0 + lane < nsplit ? part_lse[row_of(s0 + lane)] : kNegInf);
@@ -495,7 +518,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   for (int s0 = 0; s0 < nsplit; s0 += 64) {
     const int my = s0 + lane;
     const float w_l = my < nsplit ? fast_exp2(part_lse[row_of(my)] - mx) : 0.f;
-    const int64_t row_l = my < nsplit ? row_of(my) : 0;
     wsum += w_l;
     const int cnt = min(64, nsplit - s0);
     // 16 splits' loads in flight at a time: a long row's merge is a chain of
@@ -504,10 +526,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     for (; s + 16 <= cnt; s += 16) {
       float2 v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t r = __shfl(row_l, s + i);
-        v[i] = *(const float2*)(part_o + r * kHeadDim + 2 * lane);
-      }
+      for (int i = 0; i < 16; ++i)
+        v[i] = *(const float2*)(part_o + row_of(s0 + s + i) * kHeadDim + 2 * lane);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float w = __shfl(w_l, s + i);
@@ -516,15 +536,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
       }
     }
     for (; s < cnt; ++s) {
-      const int64_t r = __shfl(row_l, s);
-      const float2 v = *(const float2*)(part_o + r * kHeadDim + 2 * lane);
+      const float2 v = *(const float2*)(part_o + row_of(s0 + s) * kHeadDim + 2 * lane);
       const float w = __shfl(w_l, s);
       acc0 += w * v.x;
       acc1 += w * v.y;
     }
   }
   const float inv = 1.f / wave_sum(wsum);
-  uint32_t* dst = (uint32_t*)(out + ((int64_t)b * num_q_heads + h) * kHeadDim);
   dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
 }
 
@@ -581,7 +599,10 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !plan.splits) return err;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.num_q_heads, a.batch), dim3(64), 0, stream,
+  const int64_t merge_rows = (int64_t)a.batch * a.num_q_heads;
+  hipLaunchKernelGGL(decode_merge_kernel,
+                     dim3((unsigned)((merge_rows + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(64 * kMergeWaves), 0, stream,
                      k.part_o, k.part_lse, a.seq_lens, k.req_blocks, (uint16_t*)a.out, a.batch,
                      a.num_q_heads, a.num_kv_heads, a.max_seq_len, plan.waves);
   return hipGetLastError();
