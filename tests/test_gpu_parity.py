@@ -107,6 +107,7 @@ def test_decode_tp4_part():
     (16, 1, 3, [5, 100, 301]),               # G=16, non power-of-two page size
     (10, 2, 16, [16, 17, 1000, 4097]),       # G=5
     (16, 2, 64, [1, 64, 65, 9000]),          # G=8
+    (16, 2, 96, [95, 96, 97, 3000]),         # G=8, pages of 96 slots (not a power of two)
 ])
 def test_decode_edge_shapes(hq, hkv, page_size, lens):
     pages = sum(-(-L // page_size) for L in lens) + 8
@@ -125,6 +126,23 @@ def test_decode_max_batch():
                         seed=25, device="cuda")
     run_decode_case(step, "max batch 4096, 16q/2kv, L in [1, 200]",
                     requests=list(range(0, 4096, 37)) + [4095])
+
+
+def test_decode_keys_past_max_seq_len_are_not_attended():
+    """A request longer than the max_seq_len hint attends only its first max_seq_len
+    keys (the documented clamp): the same as the oracle on the truncated length."""
+    step = W.build_step("clamp", 16, 2, 1, 2048, [W.decode_spec([100, 900, 700])], seed=27,
+                        device="cuda")
+    host = HostInputs(step)
+    check_store(step, host, "clamp")
+    announce("decode with seq_lens above the max_seq_len hint")
+    out = host_u16(gpu_part(step, step.parts[0], max_seq_len=640))
+    torch.cuda.synchronize()
+    part = step.parts[0]
+    clamped = np.minimum(part.seq_lens, 640).astype(np.int32)
+    ref = oracle.decode_ref(host.q[0], host.k_pool, host.v_pool, part.page_table, clamped,
+                            step.page_size, step.scale)
+    assert_close(out, ref, "decode clamped to max_seq_len")
 
 
 def test_decode_single_key_is_v_exactly():
@@ -205,6 +223,7 @@ def run_prefill_case(step, what, part_idx=0, windows=None):
     (16, 1, 3, [7, 100], [45, 130]),                     # G=16, P=3
     (40, 8, 64, [4096, 0, 130], [33, 257, 64]),          # 14B heads, P=64
     (16, 2, 128, [200, 0], [100, 300]),                  # pages longer than a key tile
+    (16, 2, 96, [500, 31], [70, 200]),                   # 96-slot pages
 ])
 def test_prefill_edge_shapes(hq, hkv, page_size, prefix, extend):
     seq = np.add(prefix, extend)
