@@ -162,7 +162,8 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
  *                 (may be NULL when that size is 0); it holds the dispatch order of the
  *                 launch's work items, written by the launch itself
  * Supported: D == 128. Requests with e_b == 0 produce no rows. batch == 0 or
- * num_tokens == 0 is a no-op.
+ * num_tokens == 0 is a no-op. max_extend sets how many 256-row q tiles each request
+ * gets: output rows of new tokens past max_extend may be left unwritten.
  */
 int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* page_table,
