@@ -307,20 +307,34 @@ void prefill_kernel(PrefillKernelArgs p) {
   // Issue the K/V loads of the tile at kt into `stage` from its page-table entries in
   // ring slot `slot`. A page id outside the pool reads slot 0 (that request's result
   // is then unspecified); every access stays in bounds.
+  const uint32_t pages_u = (uint32_t)p.pg.num_pages;  // slots (so pages) < 2^31
+  const uint32_t row_bytes = (uint32_t)row_elems * 2u;
   auto dma_tile = [&](int kt, int stage, int slot) {
     const i32x4 page = *(const i32x4*)&ids_lds[slot][wave][4 * (lane >> 4)];
     uint16_t* kd = k_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
     uint16_t* vd = v_lds + stage * kTileElems + kKeysPerWave * wave * kHeadDim;
+    uint32_t slot_i[4];
+    if (p.pg.page_shift >= 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        slot_i[i] = ((uint32_t)page[i] << p.pg.page_shift) +
+                    (uint32_t)(dma_key(kt, i) & (p.pg.page_size - 1));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = dma_key(kt, i);
+        slot_i[i] = (uint32_t)page[i] * p.pg.page_size +
+                    (uint32_t)(key - page_index(key, p.pg) * p.pg.page_size);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = dma_key(kt, i);
-      const int off = key - page_index(key, p.pg) * p.pg.page_size;
-      const int32_t slot_i =
-          (uint32_t)page[i] < (uint64_t)p.pg.num_pages ? page[i] * p.pg.page_size + off : 0;
-      const int64_t row = (int64_t)slot_i * row_elems;
+      const uint64_t ro = (uint64_t)((uint32_t)page[i] < pages_u ? slot_i[i] : 0u) * row_bytes;
       const int rr = (4 * i + (lane >> 4)) & 15;  // key row mod 16 (16w is a multiple of 16)
-      global_to_lds(kbase + row + 8 * ((lane & 15) ^ rr), kd + 4 * i * kHeadDim);
-      global_to_lds(vbase + row + 8 * ((lane & 15) ^ (2 * (rr & 7))), vd + 4 * i * kHeadDim);
+      global_to_lds((const uint16_t*)((const char*)(kbase + 8 * ((lane & 15) ^ rr)) + ro),
+                    kd + 4 * i * kHeadDim);
+      global_to_lds((const uint16_t*)((const char*)(vbase + 8 * ((lane & 15) ^ (2 * (rr & 7)))) + ro),
+                    vd + 4 * i * kHeadDim);
     }
   };
 
