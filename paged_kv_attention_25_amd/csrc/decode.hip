@@ -20,12 +20,13 @@
 // Nothing synchronises the wavefronts, and moving to the next segment reads only LDS.
 //
 // Streaming. A wavefront holds one 64-key block (32 KB of K/V at 256-byte head
-// rows) in registers. After computing a block it issues the loads of the next block
-// - possibly in the next segment - then moves its cursor (LDS only) and issues the
-// page-table entries of the block after that (one entry per lane covers 64 keys).
-// Page-table entries are consumed only after the next compute, so waiting for them
-// never drains K/V loads issued after them (vmcnt counts vector memory operations
-// in issue order).
+// rows) in registers. The next block's K (and q) go out as soon as this block's
+// scores are computed, its V as soon as this block's PV is done (each into the
+// registers just freed); the wavefront then moves its cursor (LDS only) and issues
+// the page-table entries of the block after that (one entry per lane covers 64 keys).
+// Page-table entries are consumed only after the next block's scores, so waiting for
+// them never drains K/V loads issued after them (vmcnt counts vector memory
+// operations in issue order).
 //
 // Per block, the G q heads of kv head g are the columns of 16x16x32 bf16 MFMA
 // tiles (padded to 16 with zero queries):
@@ -211,37 +212,42 @@ __device__ __forceinline__ int32_t resolve(RawSlot r, const DecodeKernelArgs& p)
   return ok ? r.page * p.pg.page_size + r.off : -1;
 }
 
-// Issue the loads of one block. `slot` is this lane's slot of key (block start +
-// lane). A key whose page id is outside the pool (slot -1) reads slot 0 instead: the
+// Issue the loads of one block: K and q (kKQ) and/or V (kV). `slot` is this lane's
+// slot of key (block start + lane). A key whose page id is outside the pool (slot -1) reads slot 0 instead: the
 // access stays in bounds and that request's result is unspecified.
+template <bool kKQ, bool kV>
 __device__ __forceinline__ void load_block(Block& blk, const Desc& d, int32_t slot, int n, int grp,
                                            const DecodeKernelArgs& p) {
   const int64_t row_elems = (int64_t)p.num_kv_heads * kHeadDim;
   const uint16_t* kbase = p.k_pool + (int64_t)d.g * kHeadDim + 8 * grp;
   const uint16_t* vbase = p.v_pool + (int64_t)d.g * kHeadDim + 8 * n;
-  if (n < p.group) {
-    const uint16_t* qrow =
-        p.q + ((int64_t)d.b * p.num_q_heads + d.g * p.group + n) * kHeadDim + 8 * grp;
+  if (kKQ) {
+    if (n < p.group) {
+      const uint16_t* qrow =
+          p.q + ((int64_t)d.b * p.num_q_heads + d.g * p.group + n) * kHeadDim + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) blk.q[c] = *(const u32x4*)(qrow + 32 * c);
-  } else {
+      for (int c = 0; c < 4; ++c) blk.q[c] = *(const u32x4*)(qrow + 32 * c);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) blk.q[c] = u32x4{0, 0, 0, 0};
+      for (int c = 0; c < 4; ++c) blk.q[c] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int32_t sk = max(__shfl(slot, 16 * s + n), 0);
+      const uint16_t* kp = kbase + (int64_t)sk * row_elems;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) blk.k[s][c] = *(const u32x4*)(kp + 32 * c);
+    }
   }
+  if (kV) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int32_t sk = max(__shfl(slot, 16 * s + n), 0);
-    const uint16_t* kp = kbase + (int64_t)sk * row_elems;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) blk.k[s][c] = *(const u32x4*)(kp + 32 * c);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kl = 32 * h + ((j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4)));
-      const int32_t sv = max(__shfl(slot, kl), 0);
-      blk.v[h][j] = *(const u32x4*)(vbase + (int64_t)sv * row_elems);
+      for (int j = 0; j < 8; ++j) {
+        const int kl = 32 * h + ((j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4)));
+        const int32_t sv = max(__shfl(slot, kl), 0);
+        blk.v[h][j] = *(const u32x4*)(vbase + (int64_t)sv * row_elems);
+      }
     }
   }
 }
@@ -253,8 +259,11 @@ __device__ __forceinline__ void reset_state(SoftmaxState& st) {
   for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-__device__ __forceinline__ void compute_block(const Block& blk, const Desc& d, int grp,
-                                              float scale_log2, SoftmaxState& st) {
+// Scores and softmax of one block (K and q only): P^T operands in pb, running state
+// updated (O rescaled).
+__device__ __forceinline__ void scores_softmax(const Block& blk, const Desc& d, int grp,
+                                               float scale_log2, SoftmaxState& st,
+                                               u32x4 (&pbs)[2]) {
   // Scores: lane holds column n (q head), keys k0 + 16s + 4*grp + v in sacc[s][v].
   f32x4 sacc[4];
 #pragma unroll
@@ -292,11 +301,19 @@ __device__ __forceinline__ void compute_block(const Block& blk, const Desc& d, i
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // P^T operand of half h: slots j<4 -> group 2h, j>=4 -> group 2h+1
-    u32x4 pb;
-    pb[0] = pack_bf16x2(pr[8 * h + 0], pr[8 * h + 1]);
-    pb[1] = pack_bf16x2(pr[8 * h + 2], pr[8 * h + 3]);
-    pb[2] = pack_bf16x2(pr[8 * h + 4], pr[8 * h + 5]);
-    pb[3] = pack_bf16x2(pr[8 * h + 6], pr[8 * h + 7]);
+    pbs[h][0] = pack_bf16x2(pr[8 * h + 0], pr[8 * h + 1]);
+    pbs[h][1] = pack_bf16x2(pr[8 * h + 2], pr[8 * h + 3]);
+    pbs[h][2] = pack_bf16x2(pr[8 * h + 4], pr[8 * h + 5]);
+    pbs[h][3] = pack_bf16x2(pr[8 * h + 6], pr[8 * h + 7]);
+  }
+}
+
+// O^T += V^T P^T for one block (V only).
+__device__ __forceinline__ void pv_block(const Block& blk, const u32x4 (&pbs)[2],
+                                         SoftmaxState& st) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 pb = pbs[h];
     const u32x4* vv = blk.v[h];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -418,16 +435,20 @@ void decode_split_kernel(DecodeKernelArgs p) {
   reset_state(st);
   Block blk;
   Desc d = cursor_next(cur, wave_id, p, lds);
-  load_block(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
+  load_block<true, true>(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
   Desc dn = cursor_next(cur, wave_id, p, lds);
   RawSlot raw_n = lookup_raw(dn, lane, p);
 
   while (d.valid) {
-    compute_block(blk, d, grp, p.scale_log2, st);
-    // The next block's loads go out first; the cursor (LDS only), the page-table
-    // entries of the block after and this segment's stores follow.
+    // The next block's K and q go out as soon as this block's scores are computed, its
+    // V as soon as this block's PV is done; then the cursor (LDS only), the page-table
+    // entries of the block after and this segment's stores.
+    u32x4 pbs[2];
+    scores_softmax(blk, d, grp, p.scale_log2, st, pbs);
     const int32_t slot_n = resolve(raw_n, p);
-    if (dn.valid) load_block(blk, dn, slot_n, n, grp, p);
+    if (dn.valid) load_block<true, false>(blk, dn, slot_n, n, grp, p);
+    pv_block(blk, pbs, st);
+    if (dn.valid) load_block<false, true>(blk, dn, slot_n, n, grp, p);
     const Desc dnn = cursor_next(cur, wave_id, p, lds);
     raw_n = lookup_raw(dnn, lane, p);
     if (d.last) finish_segment(d, st, n, grp, p);
