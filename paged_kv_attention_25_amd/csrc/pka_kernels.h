@@ -21,10 +21,12 @@ struct StoreArgs {
 };
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t stream);
 
-// Plan of the decode kernel: `waves` wavefronts share the batch's 64-key blocks
-// (equal contiguous ranges); `splits` when a (request, kv head) pair can have two or
-// more blocks and so be split between wavefronts (then a merge pass runs).
+// Plan of the decode kernel: `groups` groups of Hkv wavefronts (`waves` in all) share
+// the batch's 64-key blocks, each group an equal contiguous range of the requests'
+// blocks, one wavefront per kv head; `splits` when a (request, kv head) pair can have
+// two or more blocks and so be split between groups (then a merge pass runs).
 struct DecodePlan {
+  int32_t groups;
   int32_t waves;
   bool splits;
 };

@@ -108,6 +108,8 @@ def test_decode_tp4_part():
     (10, 2, 16, [16, 17, 1000, 4097]),       # G=5
     (16, 2, 64, [1, 64, 65, 9000]),          # G=8
     (16, 2, 96, [95, 96, 97, 3000]),         # G=8, pages of 96 slots (not a power of two)
+    (12, 3, 1, [70, 2000, 4000, 129]),       # 3 kv heads: 682 groups of 3 wavefronts
+    (16, 16, 16, [1, 300, 5000]),            # 16 kv heads, G=1: 128 groups of 16
 ])
 def test_decode_edge_shapes(hq, hkv, page_size, lens):
     pages = sum(-(-L // page_size) for L in lens) + 8
