@@ -6,8 +6,10 @@
 Prints ONE JSON line. The headline workload is the offline-style decode batch
 (Qwen3-0.6B heads 16q/8kv, d=128, bf16, batch 256, context lengths uniform in
 [200, 2048], page size 1, slots scattered over a 2^20-slot pool). One step is the
-whole decode step of the path: store_kv of the 256 new tokens, then the split
-decode kernel and its merge pass. `value` is the step's algorithmic HBM bytes
+whole decode step of the path: the store of the 256 new tokens' K/V rows and the
+decode over all keys, made by pka_paged_attn_decode_store (the split decode kernel
+with the store inside, then its merge pass); the same step as store_kv followed by
+the decode call is timed beside it. `value` is the step's algorithmic HBM bytes
 (K+V of every attended token, q, out, page-table entries and seq_lens, plus the
 store's reads and writes) divided by the step's time, with inputs resident in
 HBM and the caches flushed (a 1 GiB read) before every timed step.
@@ -19,7 +21,9 @@ under "parts": decode in GB/s against the 8 TB/s HBM peak, prefill in TFLOP/s
 dense bf16 MFMA peak.
 
 Times come from HIP events recorded on the stream the kernels run on (torch's
-current stream, which the binding passes to every call). The oracle (float64,
+current stream, which the binding passes to every call): a step's time between one
+event before it and one after it; the per-call breakdown (store, decode, prefill) in a
+second pass with an event after every call. The oracle (float64,
 numpy, one BLAS thread) is timed on the host over the full decode batch as
 "cpu_baseline".
 """
@@ -82,13 +86,17 @@ def source_hash(*names):
 
 
 class Runner:
-    """Device-resident metadata and closures for one workload step."""
+    """Device-resident metadata and closures for one workload step. With `fused`, a
+    decode-only step stores its new rows inside the decode launch
+    (pka_paged_attn_decode_store) instead of a store_kv call before it."""
 
-    def __init__(self, step):
+    def __init__(self, step, fused=False):
         import torch
         import paged_kv_attention_25_amd as pka
         self.step = step
         self.pka = pka
+        self.fused = (fused and len(step.parts) == 1 and step.parts[0].kind == "decode"
+                      and step.parts[0].batch == step.out_loc.size)
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
         self.out_loc = i32(step.out_loc)
         self.meta = []
@@ -111,12 +119,19 @@ class Runner:
             self.meta.append(m)
 
     def store(self):
+        if self.fused:
+            return
         s = self.step
         self.pka.store_kv(s.k_new, s.v_new, self.out_loc, s.k_pool, s.v_pool, s.page_size)
 
     def attend(self, i):
         s, part, m = self.step, self.step.parts[i], self.meta[i]
-        if part.kind == "decode":
+        if part.kind == "decode" and self.fused:
+            self.pka.paged_attn_decode_store(part.q, s.k_new, s.v_new, self.out_loc, s.k_pool,
+                                             s.v_pool, m["pt"], m["seq"], part.max_seq_len,
+                                             s.page_size, s.scale, out=m["out"],
+                                             workspace=m["ws"])
+        elif part.kind == "decode":
             self.pka.paged_attn_decode(part.q, s.k_pool, s.v_pool, m["pt"], m["seq"],
                                        part.max_seq_len, s.page_size, s.scale, out=m["out"],
                                        workspace=m["ws"])
@@ -130,20 +145,36 @@ PART_WARMUP = 60  # warmup steps of the workloads reported under "parts"
 
 
 def time_step(runner, steps, warmup, flush, cold=True):
-    """Run warmup steps, then `steps` timed steps. Each timed step records HIP events
-    between its calls (store, then each attention part) on the current stream; a cache
-    flush runs before each timed step, outside the events. Returns the per-segment
-    median ms over the timed steps, their sum, and the wall time of the bracketed
-    region."""
+    """Run warmup steps, then time `steps` steps twice. Pass 1 records one HIP event
+    before and one after each step (the step's time: an event marker between calls
+    holds the stream for a few µs, so none is placed inside the step). Pass 2 records
+    an event after every call (store, then each attention part) for the per-call
+    breakdown. A cache flush runs before each timed step, outside the events. Returns
+    the per-call medians (ms, pass 2), the median step time (ms, pass 1) and the wall
+    time of pass 1."""
     import torch
     nparts = len(runner.step.parts)
-    for _ in range(warmup):
+
+    def calls():
         runner.store()
         for i in range(nparts):
             runner.attend(i)
+
+    for _ in range(warmup):
+        calls()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nparts + 2)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
+    for k in range(steps):
+        if cold:
+            flush()
+        ev[k][0].record()
+        calls()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nparts + 2)] for _ in range(steps)]
     for k in range(steps):
         if cold:
             flush()
@@ -155,10 +186,9 @@ def time_step(runner, steps, warmup, flush, cold=True):
             runner.attend(i)
             e[i + 2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_step = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nparts + 1)] for e in evs])
     seg = np.median(per_step, axis=0)
-    return seg, float(seg.sum()), wall
+    return seg, total, wall
 
 
 def graph_step_us(runner, steps, flush):
@@ -280,7 +310,7 @@ def write_traffic(fetch_dir, write_dir):
     w_split, w_merge = mean_of(write, "decode_split_kernel"), mean_of(write, "decode_merge_kernel")
     total = ((f_split + f_merge) * fetch_scale + (w_split + w_merge) * write_scale) * kib
     rec = {"source_hash": source_hash("decode.hip", "pka_device.h"), "workload": "decode_b256",
-           "kernels": "decode_split_kernel + decode_merge_kernel",
+           "kernels": "decode_split_kernel<true> (decode with the store) + decode_merge_kernel",
            "bytes_per_launch": int(round(total)),
            "fetch_kib": {"split": round(f_split, 1), "merge": round(f_merge, 1)},
            "write_kib": {"split": round(w_split, 1), "merge": round(w_merge, 1)},
@@ -319,15 +349,22 @@ def time_part(name, steps, warmup, flush, log):
     from paged_kv_attention_25_amd import workloads as W
     log(f"{name}: generating inputs")
     st = W.WORKLOADS[name](device="cuda", fill="zero")
-    r = Runner(st)
+    r = Runner(st, fused=True)
     torch.cuda.synchronize()
     seg, tot, _ = time_step(r, steps, warmup, flush)
-    rec = {"step_us": round(tot * 1e3, 2), "store_us": round(seg[0] * 1e3, 2),
-           "store_GBs": round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1)}
+    rec = {"step_us": round(tot * 1e3, 2)}
+    if r.fused:
+        rec["store"] = "inside the decode launch (pka_paged_attn_decode_store)"
+    else:
+        rec.update(store_us=round(seg[0] * 1e3, 2),
+                   store_GBs=round(store_bytes(st) / (seg[0] * 1e-3) / 1e9, 1))
     for i, p in enumerate(st.parts):
-        us = seg[i + 1] * 1e3
+        # a fused step is its one decode call: its time is the step's (no event inside)
+        us = tot * 1e3 if r.fused else seg[i + 1] * 1e3
         if p.kind == "decode":
-            gbs = decode_bytes(p, st) / (us * 1e-6) / 1e9
+            # the fused launch also moves the store's bytes
+            nbytes = decode_bytes(p, st) + (store_bytes(st) if r.fused else 0)
+            gbs = nbytes / (us * 1e-6) / 1e9
             rec["decode_us"] = round(us, 2)
             rec["decode_GBs"] = round(gbs, 1)
             rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
@@ -337,6 +374,11 @@ def time_part(name, steps, warmup, flush, log):
             rec["prefill_TFLOPs"] = round(tf, 1)
             rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
             rec["prefill_flops"] = prefill_flops(p, st)
+    if r.fused:
+        ru = Runner(st)
+        _, tot_u, _ = time_step(ru, steps, warmup, flush)
+        rec["unfused_step_us"] = round(tot_u * 1e3, 2)   # store_kv, then decode
+        del ru
     if name == "tiny_decode":
         rec["graph_step_us"] = round(graph_step_us(r, steps, flush), 2)
     log(f"{name}: {rec}")
@@ -398,21 +440,25 @@ def main():
     # --- headline: decode_b256 ------------------------------------------------------
     log("decode_b256: generating inputs")
     step = W.decode_b256(device="cuda", fill="zero")
-    run = Runner(step)
+    run = Runner(step, fused=True)
     part = step.parts[0]
     torch.cuda.synchronize()
     seg, total_ms, wall = time_step(run, args.steps, args.warmup, flush)
     dec_bytes = decode_bytes(part, step)
     st_bytes = store_bytes(step)
     value = (dec_bytes + st_bytes) / (total_ms * 1e-3) / 1e9
-    dec_gbs = dec_bytes / (seg[1] * 1e-3) / 1e9
-    log(f"decode_b256: step {total_ms*1e3:.1f} us (store {seg[0]*1e3:.1f}, decode "
-        f"{seg[1]*1e3:.1f}); decode {dec_gbs:.0f} GB/s")
+    # the launch stores and decodes: its algorithmic bytes are both
+    launch_bytes = dec_bytes + st_bytes
+    launch_ms = total_ms   # the step is the one decode_store call (split + merge)
+    dec_gbs = launch_bytes / (launch_ms * 1e-3) / 1e9
+    log(f"decode_b256: step {total_ms*1e3:.1f} us; {dec_gbs:.0f} GB/s")
     khash = source_hash("decode.hip", "pka_device.h")
-    roofline = {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
+    roofline = {"bound": "hbm",
+                "kernel": "decode_split_kernel<store> + decode_merge_kernel",
                 "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(khash),
-                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(seg[1] * 1e3, 2)}
+                "algorithmic_bytes_per_launch": launch_bytes,
+                "avg_launch_us": round(launch_ms * 1e3, 2)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 4),
@@ -420,7 +466,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/k/v; lengths and page permutations seeded)",
         "config": {"workload": "decode_b256: Qwen3-0.6B heads 16q/8kv, d=128, batch 256, "
                                "context U[200,2048], page_size 1, 2^20-slot pool; "
-                               "step = store_kv(256) + split decode + merge",
+                               "step = decode_store (split decode with the store of the 256 "
+                               "new rows inside) + merge",
                    "batch": part.batch, "sum_context": int(part.seq_lens.sum()),
                    "timing": "HIP events on the launch stream, caches flushed before each step; "
                              "median over the timed steps",
@@ -430,8 +477,18 @@ def main():
     if args.calibration_copy:
         calibration_copy(flush)
     if args.hot:
-        seg_h, tot_h, _ = time_step(run, args.steps, 0, flush, cold=False)
-        result["config"]["hot_cache_decode_GBs"] = round(dec_bytes / (seg_h[1] * 1e-3) / 1e9, 1)
+        _, tot_h, _ = time_step(run, args.steps, 0, flush, cold=False)
+        result["config"]["hot_cache_decode_GBs"] = round(launch_bytes / (tot_h * 1e-3) / 1e9, 1)
+    if not args.quick:
+        # the same step as two calls: store_kv, then the decode
+        run_u = Runner(step)
+        seg_u, tot_u, _ = time_step(run_u, args.steps, args.warmup, flush)
+        result["config"]["unfused_step"] = {
+            "step_us": round(tot_u * 1e3, 2),
+            "value_GBs": round((dec_bytes + st_bytes) / (tot_u * 1e-3) / 1e9, 1),
+            "with_an_event_after_each_call": {"store_us": round(seg_u[0] * 1e3, 2),
+                                              "decode_us": round(seg_u[1] * 1e3, 2)}}
+        del run_u
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on decode_b256")

@@ -8,6 +8,8 @@
  *   pka_paged_attn_prefill  causal extend (chunked) prefill on top of a cached prefix
  *   pka_paged_attn_decode   batched GQA decode, split over the key axis, then merged
  *
+ * and pka_paged_attn_decode_store, a decode step's store and decode in one launch.
+ *
  * The pages this follows describe a pool shared by all requests whose
  * allocation unit is a page of page_size tokens (default 1) ["Mini-SGLang
  * deployment guide" (dpshk.com), section 6.2 "Page Size" and section 6.5 "Radix
@@ -137,6 +139,34 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
 
 /* Workspace bytes pka_paged_attn_decode needs for this geometry and plan. */
 size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t max_seq_len);
+
+/*
+ * pka_paged_attn_decode_store - the decode step's store and decode in one launch.
+ *
+ * The same result as pka_store_kv(k_new, v_new, out_loc, batch) followed by
+ * pka_paged_attn_decode on the same stream, for a decode step whose one new token per
+ * request has just been given a slot [deployment guide, sections 6.2-6.4]: the new
+ * token's K/V rows are written to the pools and attended in the same pass.
+ *
+ *   k_new, v_new  [batch, Hkv, D] bf16 (device): request b's new token's rows
+ *   out_loc       [batch] int32 (device): slot of request b's new token. A slot outside
+ *                 [0, num_pages*P) is skipped, as in pka_store_kv.
+ *   k_pool, v_pool  the pools (device), read and updated in place
+ *   other arguments, workspace size and support as in pka_paged_attn_decode.
+ * Where the page table maps request b's key L_b - 1 to slot out_loc[b] (the usual
+ * decode step), that key is read from k_new / v_new; every other key is read from the
+ * pools. The slots in out_loc must be pairwise distinct and must not be read as another
+ * request's keys in the same call (new tokens' slots are private to their request);
+ * then the result equals the two calls' bit for bit in the pools and within rounding
+ * order in out. The store of request b is made by the wavefront that reads its last
+ * key block, so it needs L_b >= 1 (as decode does).
+ */
+int pka_paged_attn_decode_store(const pka_geom* geom, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* out_loc, void* k_pool,
+                                void* v_pool, const int32_t* page_table,
+                                int32_t page_table_stride, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pka_paged_attn_prefill - causal extend prefill on top of a cached prefix.

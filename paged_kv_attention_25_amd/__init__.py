@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "pka_status_string",
     "pka_store_kv",
     "pka_paged_attn_decode",
+    "pka_paged_attn_decode_store",
     "pka_decode_workspace_bytes",
     "pka_paged_attn_prefill",
     "pka_prefill_workspace_bytes",
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.pka_paged_attn_decode.restype = ctypes.c_int
     L.pka_paged_attn_decode.argtypes = [gp, vp, vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, sz,
                                         vp]
+    L.pka_paged_attn_decode_store.restype = ctypes.c_int
+    L.pka_paged_attn_decode_store.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                              f32, vp, vp, sz, vp]
     L.pka_decode_workspace_bytes.restype = sz
     L.pka_decode_workspace_bytes.argtypes = [gp, i32, i32]
     L.pka_paged_attn_prefill.restype = ctypes.c_int
@@ -171,6 +175,30 @@ def paged_attn_decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, page
                                        _ptr(seq_lens), batch, int(max_seq_len), float(scale),
                                        _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(q.device)), "pka_paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_store(q, k_new, v_new, out_loc, k_pool, v_pool, page_table, seq_lens,
+                            max_seq_len, page_size, scale, out=None, workspace=None):
+    """pka_paged_attn_decode_store: stores k_new[b], v_new[b] [B, Hkv, D] into slot
+    out_loc[b] of the pools and decodes, in one launch (the same result as store_kv then
+    paged_attn_decode). Returns out [B, Hq, D]."""
+    import torch
+    g = _pool_geom(q.shape[1], k_pool, page_size)
+    batch = int(q.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(lib().pka_decode_workspace_bytes(ctypes.byref(g), batch, int(max_seq_len)))
+    if workspace is None and need > 0:
+        workspace = _alloc_like(q, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pka_paged_attn_decode_store(ctypes.byref(g), _ptr(q), _ptr(k_new),
+                                             _ptr(v_new), _ptr(out_loc), _ptr(k_pool),
+                                             _ptr(v_pool), _ptr(page_table),
+                                             int(page_table.shape[1]), _ptr(seq_lens), batch,
+                                             int(max_seq_len), float(scale), _ptr(out),
+                                             _ptr(workspace), ws_bytes, _stream(q.device)),
+           "pka_paged_attn_decode_store")
     return out
 
 

@@ -74,11 +74,22 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
   return pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
 }
 
-int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
-                          const void* v_pool, const int32_t* page_table,
-                          int32_t page_table_stride, const int32_t* seq_lens, int32_t batch,
-                          int32_t max_seq_len, float scale, void* out, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the decode entry points; `store` non-null adds the
+// new tokens' store (k_new, v_new, out_loc) to the launch.
+struct NewRows {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* out_loc;
+};
+
+int decode_impl(const pka_geom* geom, const void* q, const void* k_pool, const void* v_pool,
+                const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                int32_t batch, int32_t max_seq_len, float scale, void* out, void* workspace,
+                size_t workspace_bytes, void* stream, const NewRows* store) {
   if (!geom) return PKA_E_NULLPTR;
   const int gs = attn_geom_status(geom);
   if (gs != PKA_OK) return gs;
@@ -91,6 +102,7 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
   const int64_t pages_needed = ((int64_t)max_seq_len + geom->page_size - 1) / geom->page_size;
   if (page_table_stride < pages_needed) return PKA_E_SHAPE;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return PKA_E_NULLPTR;
+  if (store && (!store->k_new || !store->v_new || !store->out_loc)) return PKA_E_NULLPTR;
   const pka::DecodePlan plan = pka::plan_decode(batch, geom->num_kv_heads, group, max_seq_len);
   const size_t need =
       pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
@@ -111,7 +123,38 @@ int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_poo
   a.num_kv_heads = geom->num_kv_heads;
   a.max_seq_len = max_seq_len;
   a.scale = scale;
+  if (store) {
+    a.k_new = store->k_new;
+    a.v_new = store->v_new;
+    a.out_loc = store->out_loc;
+    a.k_dst = const_cast<void*>(k_pool);
+    a.v_dst = const_cast<void*>(v_pool);
+  }
   return launch_status(pka::launch_decode(a, plan, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* page_table,
+                          int32_t page_table_stride, const int32_t* seq_lens, int32_t batch,
+                          int32_t max_seq_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_impl(geom, q, k_pool, v_pool, page_table, page_table_stride, seq_lens, batch,
+                     max_seq_len, scale, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int pka_paged_attn_decode_store(const pka_geom* geom, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* out_loc, void* k_pool,
+                                void* v_pool, const int32_t* page_table,
+                                int32_t page_table_stride, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const NewRows rows{k_new, v_new, out_loc};
+  return decode_impl(geom, q, k_pool, v_pool, page_table, page_table_stride, seq_lens, batch,
+                     max_seq_len, scale, out, workspace, workspace_bytes, stream, &rows);
 }
 
 size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,

@@ -84,6 +84,14 @@ struct DecodeKernelArgs {
   int32_t max_seq_len;  // keys past it are not attended
   int32_t groups;       // C: groups of Hkv wavefronts sharing the blocks
   float scale_log2;
+  // Store of the new tokens' rows (null k_new: none): request b's row goes to slot
+  // out_loc[b] of k_dst / v_dst (the pools).
+  const uint16_t* __restrict__ k_new;  // [B, Hkv, D]
+  const uint16_t* __restrict__ v_new;
+  const int32_t* __restrict__ out_loc;  // [B]
+  uint16_t* k_dst;
+  uint16_t* v_dst;
+  int64_t num_slots;
 };
 
 struct Lds {
@@ -106,6 +114,7 @@ struct Desc {
   int32_t k0, end, L;  // block start key, end of its segment's keys, request length
   int32_t last;        // last block of its segment
   int32_t slot;        // partial-output slot of its segment, or -1: written directly
+  int32_t tail;        // the block holds the request's key L - 1 (its pair's last block)
 };
 
 struct SoftmaxState {
@@ -169,11 +178,13 @@ __device__ __forceinline__ Desc cursor_next(Cursor& c, int32_t wave_id, const De
   if (!d.valid) {
     d.k0 = d.end = 0;
     d.last = 0;
+    d.tail = 0;
     return d;
   }
   d.k0 = c.j * kBlock;
   d.end = min(c.L, (c.j + (c.seg_end - c.x)) * kBlock);
   d.last = c.x + 1 >= c.seg_end;
+  d.tail = d.end == c.L && c.L <= d.k0 + kBlock;
   c.x += 1;
   c.j += 1;
   if (c.x >= c.seg_end && c.x < c.hi) locate(c, wave_id, p, lds);
@@ -185,13 +196,30 @@ __device__ __forceinline__ Desc cursor_next(Cursor& c, int32_t wave_id, const De
 struct RawSlot {
   int32_t page;  // loaded page id
   int32_t off;   // offset in the page; -1 when the key's table index is past the row
+  // (store, the pair's last block) the request's out_loc and this lane's 4 bytes of
+  // the new token's K and V rows of kv head g
+  int32_t loc;
+  uint32_t krow, vrow;
 };
 
+template <bool kStore>
 __device__ __forceinline__ RawSlot lookup_raw(const Desc& d, int lane, const DecodeKernelArgs& p) {
   RawSlot r;
   r.page = 0;
   r.off = -1;
+  r.loc = -1;
+  r.krow = r.vrow = 0u;
   if (!d.valid) return r;
+  if (kStore && d.tail) {
+    r.loc = p.out_loc[d.b];
+    // (lane offset hidden from the compiler: per-lane pointers formed outside the
+    // loop would cost registers for the whole stream)
+    int32_t lo = 2 * lane;
+    asm volatile("" : "+v"(lo));
+    const int64_t e = ((int64_t)d.b * p.num_kv_heads + d.g) * kHeadDim;
+    r.krow = *(const uint32_t*)(p.k_new + e + lo);
+    r.vrow = *(const uint32_t*)(p.v_new + e + lo);
+  }
   // keys past the block's end are clamped to the last valid key (loaded, masked)
   const int32_t key = min(d.k0 + lane, d.end - 1);
   int32_t idx;
@@ -214,6 +242,25 @@ __device__ __forceinline__ int32_t resolve(RawSlot r, const DecodeKernelArgs& p)
   hold(r.page);
   const bool ok = r.off >= 0 && r.page >= 0 && (int64_t)r.page < p.pg.num_pages;
   return ok ? r.page * p.pg.page_size + r.off : -1;
+}
+
+// (store) Before the loads of a pair's last block: write the new token's row of kv
+// head d.g to slot out_loc[b] when that slot is inside the pool. The wavefront's own
+// loads issued after these stores see them, so the block's key L - 1 reads the new
+// row when the page table maps it to that slot.
+__device__ __forceinline__ void store_new_row(const Desc& d, RawSlot r, int lane,
+                                              const DecodeKernelArgs& p) {
+  if (!d.tail) return;
+  hold(r.loc);
+  hold(r.krow);
+  hold(r.vrow);
+  const int32_t loc = uniform(r.loc);
+  if (loc < 0 || (int64_t)loc >= p.num_slots) return;
+  int32_t lo = 2 * lane;
+  asm volatile("" : "+v"(lo));
+  const int64_t e = ((int64_t)loc * p.num_kv_heads + d.g) * kHeadDim;
+  *(uint32_t*)(p.k_dst + e + lo) = r.krow;
+  *(uint32_t*)(p.v_dst + e + lo) = r.vrow;
 }
 
 // Issue the loads of one block: K and q (kKQ) and/or V (kV). `slot` is this lane's
@@ -343,6 +390,9 @@ __device__ __forceinline__ void pv_block(const Block& blk, const u32x4 (&pbs)[2]
 // the normalised partial output and its log2-sum-exp in the segment's slot.
 __device__ __forceinline__ void finish_segment(const Desc& d, SoftmaxState& st, int n, int grp,
                                                const DecodeKernelArgs& p) {
+  // (lane indices hidden from the compiler: output pointers formed outside the loop
+  // would hold registers for the whole stream)
+  asm volatile("" : "+v"(n), "+v"(grp));
   float ltot = st.lsum + __shfl_xor(st.lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   const float inv = 1.f / ltot;
@@ -375,7 +425,9 @@ __device__ __forceinline__ void finish_segment(const Desc& d, SoftmaxState& st, 
   reset_state(st);
 }
 
-// Two wavefronts per SIMD (256 registers each).
+// Two wavefronts per SIMD (256 registers each). kStore: the launch also stores the new
+// tokens' rows (p.k_new non-null).
+template <bool kStore>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_split_kernel(DecodeKernelArgs p) {
   __shared__ Lds lds;
@@ -441,22 +493,29 @@ void decode_split_kernel(DecodeKernelArgs p) {
   reset_state(st);
   Block blk;
   Desc d = cursor_next(cur, wave_id, p, lds);
-  load_block<true, true>(blk, d, resolve(lookup_raw(d, lane, p), p), n, grp, p);
+  {
+    const RawSlot raw = lookup_raw<kStore>(d, lane, p);
+    const int32_t slot = resolve(raw, p);
+    if (kStore) store_new_row(d, raw, lane, p);
+    load_block<true, true>(blk, d, slot, n, grp, p);
+  }
   Desc dn = cursor_next(cur, wave_id, p, lds);
-  RawSlot raw_n = lookup_raw(dn, lane, p);
+  RawSlot raw_n = lookup_raw<kStore>(dn, lane, p);
 
   while (d.valid) {
     // The next block's K and q go out as soon as this block's scores are computed, its
     // V as soon as this block's PV is done; then the cursor (LDS only), the page-table
-    // entries of the block after and this segment's stores.
+    // entries of the block after (and, with the store, the new token's row when that
+    // block is its pair's last) and this segment's stores.
     u32x4 pbs[2];
     scores_softmax(blk, d, grp, p.scale_log2, st, pbs);
     const int32_t slot_n = resolve(raw_n, p);
+    if (kStore) store_new_row(dn, raw_n, lane, p);
     if (dn.valid) load_block<true, false>(blk, dn, slot_n, n, grp, p);
     pv_block(blk, pbs, st);
     if (dn.valid) load_block<false, true>(blk, dn, slot_n, n, grp, p);
     const Desc dnn = cursor_next(cur, wave_id, p, lds);
-    raw_n = lookup_raw(dnn, lane, p);
+    raw_n = lookup_raw<kStore>(dnn, lane, p);
     if (d.last) finish_segment(d, st, n, grp, p);
     d = dn;
     dn = dnn;
@@ -628,8 +687,19 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   k.max_seq_len = a.max_seq_len;
   k.groups = plan.groups;
   k.scale_log2 = a.scale * kLog2e;
+  k.k_new = (const uint16_t*)a.k_new;
+  k.v_new = (const uint16_t*)a.v_new;
+  k.out_loc = a.out_loc;
+  k.k_dst = (uint16_t*)a.k_dst;
+  k.v_dst = (uint16_t*)a.v_dst;
+  k.num_slots = a.num_pages * (int64_t)a.page_size;
   const int grid = (plan.waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, k);
+  if (k.k_new)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0,
+                       stream, k);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0,
+                       stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !plan.splits) return err;
   const int64_t merge_rows = (int64_t)a.batch * a.num_q_heads;

@@ -53,6 +53,13 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t max_seq_len;  // keys past it are not attended
   float scale;
+  // With k_new non-null the launch also stores request b's new rows k_new[b], v_new[b]
+  // into slot out_loc[b] of k_dst / v_dst (the same pools as k_pool / v_pool).
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* out_loc = nullptr;
+  void* k_dst = nullptr;
+  void* v_dst = nullptr;
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 

@@ -43,6 +43,17 @@ def gpu_part(step, part, max_seq_len=None):
                                   step.page_size, step.scale)
 
 
+def gpu_decode_store(step, part, max_seq_len=None, out_loc=None):
+    """The fused entry: store the part's new rows and decode in one launch."""
+    r0, r1 = part.row_offset, part.row_offset + part.batch
+    loc = step.out_loc[r0:r1] if out_loc is None else out_loc
+    msl = part.max_seq_len if max_seq_len is None else max_seq_len
+    return pka.paged_attn_decode_store(part.q, step.k_new[r0:r1], step.v_new[r0:r1],
+                                       dev_i32(loc), step.k_pool, step.v_pool,
+                                       dev_i32(part.page_table), dev_i32(part.seq_lens), msl,
+                                       step.page_size, step.scale)
+
+
 class HostInputs:
     """Host copies of a step's inputs, taken before any kernel runs, and the oracle's
     own store of the new rows into its copy of the pools."""

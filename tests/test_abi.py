@@ -114,6 +114,27 @@ def test_decode_argument_errors(L):
     assert decode(L, geom(), batch=0) == pka.PKA_OK   # no-op, nothing enqueued
 
 
+def decode_store(L, g, batch=4, max_seq=250, stride=256, ws=None, ws_bytes=0, k_new=FAKE,
+                 out_loc=FAKE):
+    return L.pka_paged_attn_decode_store(ctypes.byref(g) if g is not None else None, FAKE,
+                                         k_new, FAKE, out_loc, FAKE, FAKE, FAKE, stride, FAKE,
+                                         batch, max_seq, 0.1, FAKE, ws, ws_bytes, None)
+
+
+def test_decode_store_argument_errors(L):
+    # the decode checks, plus the new rows and their slots
+    assert decode_store(L, None) == pka.PKA_E_NULLPTR
+    assert decode_store(L, geom(num_q_heads=12, num_kv_heads=8)) == pka.PKA_E_SHAPE
+    assert decode_store(L, geom(head_dim=64)) == pka.PKA_E_UNSUPPORTED
+    assert decode_store(L, geom(), batch=-1) == pka.PKA_E_SHAPE
+    assert decode_store(L, geom(), stride=100, max_seq=250) == pka.PKA_E_SHAPE
+    assert decode_store(L, geom(), k_new=None) == pka.PKA_E_NULLPTR
+    assert decode_store(L, geom(), out_loc=None) == pka.PKA_E_NULLPTR
+    assert decode_store(L, geom(), batch=32, max_seq=32768, stride=32768) == \
+        pka.PKA_E_WORKSPACE
+    assert decode_store(L, geom(), batch=0, k_new=None) == pka.PKA_OK   # no-op
+
+
 def test_prefill_argument_errors(L):
     assert prefill(L, None) == pka.PKA_E_NULLPTR
     assert prefill(L, geom(head_dim=96)) == pka.PKA_E_UNSUPPORTED

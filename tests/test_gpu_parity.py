@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from paged_kv_attention_25_amd import workloads as W
-from tests.gpu_common import (HostInputs, announce, assert_close, gpu_part, gpu_store, host_u16,
-                              oracle_decode, oracle_prefill)
+from tests.gpu_common import (HostInputs, announce, assert_close, gpu_decode_store, gpu_part,
+                              gpu_store, host_u16, oracle_decode, oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,6 +186,125 @@ def test_decode_split_count_invariance():
     assert_close(b, ref, "in a batch of 23")
     assert_close(c, ref, "alone, large max_seq_len hint")
     assert_close(a, oracle.bf16_bits_to_f64(b), "alone vs in the batch")
+
+
+# --- store and decode in one launch ------------------------------------------------------
+
+def check_pools(step, host, what):
+    assert np.array_equal(host_u16(step.k_pool), host.k_pool), f"{what}: k_pool differs"
+    assert np.array_equal(host_u16(step.v_pool), host.v_pool), f"{what}: v_pool differs"
+
+
+def run_decode_store_case(step, what, requests=None, max_seq_len=None):
+    """pka_paged_attn_decode_store on a decode-only step whose pools do not yet hold the
+    new rows (their slots are NaN): the pools must equal the oracle's store bit for bit
+    and the outputs the oracle's decode over the stored pools."""
+    host = HostInputs(step)
+    announce(f"decode+store {what}")
+    out = gpu_decode_store(step, step.parts[0], max_seq_len=max_seq_len)
+    torch.cuda.synchronize()
+    check_pools(step, host, what)
+    part = step.parts[0]
+    idx = np.arange(part.batch) if requests is None else np.asarray(requests)
+    lens = part.seq_lens[idx] if max_seq_len is None else np.minimum(part.seq_lens[idx],
+                                                                     max_seq_len)
+    ref = oracle.decode_ref(host.q[0][idx], host.k_pool, host.v_pool, part.page_table[idx],
+                            lens.astype(np.int32), step.page_size, step.scale)
+    assert_close(host_u16(out)[idx], ref, f"decode+store {what}")
+    return host, out
+
+
+def test_decode_store_tiny():
+    run_decode_store_case(W.tiny_decode(device="cuda"), "tiny_decode")
+
+
+def test_decode_store_b256_full():
+    run_decode_store_case(W.decode_b256(device="cuda"), "decode_b256 all requests")
+
+
+def test_decode_store_long_sampled():
+    run_decode_store_case(W.long_decode(device="cuda"), "long_decode (6 requests)",
+                          requests=[0, 7, 12, 19, 25, 31])
+
+
+@pytest.mark.parametrize("hq,hkv,page_size,lens", [
+    (8, 8, 1, [1, 2, 63, 64, 65, 129]),
+    (16, 1, 3, [5, 100, 301]),
+    (16, 2, 64, [1, 64, 65, 9000]),
+    (12, 3, 1, [70, 2000, 4000, 129]),
+])
+def test_decode_store_edge_shapes(hq, hkv, page_size, lens):
+    pages = sum(-(-L // page_size) for L in lens) + 8
+    step = W.build_step("edge", hq, hkv, page_size, pages, [W.decode_spec(lens)], seed=31,
+                        device="cuda")
+    run_decode_store_case(step, f"edge hq={hq} hkv={hkv} P={page_size} L={lens}")
+
+
+def test_decode_store_max_batch():
+    """4096 short requests: most wavefronts meet several pairs' last blocks (each a
+    store) in one stream."""
+    rng = np.random.default_rng(33)
+    lens = rng.integers(1, 201, size=4096)
+    step = W.build_step("max_batch", 16, 2, 1, int(lens.sum()) + 64, [W.decode_spec(lens)],
+                        seed=33, device="cuda")
+    run_decode_store_case(step, "max batch 4096", requests=list(range(0, 4096, 41)) + [4095])
+
+
+def test_decode_store_single_key_is_v_new_exactly():
+    step = W.build_step("single", 16, 8, 1, 64, [W.decode_spec([1, 1, 1])], seed=32,
+                        device="cuda")
+    host, out = run_decode_store_case(step, "single key")
+    got = host_u16(out)
+    for b in range(3):
+        for h in range(16):
+            assert np.array_equal(got[b, h], host.v_new[b, h // 2])
+
+
+def test_decode_store_past_max_seq_len():
+    """Requests longer than the max_seq_len hint still store their new rows; their
+    attention covers only the first max_seq_len keys."""
+    step = W.build_step("clamp", 16, 2, 1, 2048, [W.decode_spec([100, 900, 700])], seed=34,
+                        device="cuda")
+    run_decode_store_case(step, "seq_lens above the hint", max_seq_len=640)
+
+
+def test_decode_store_skips_out_of_pool_slots():
+    """A slot outside the pool is not written (as in store_kv); the other requests are
+    stored and decoded as usual."""
+    step = W.build_step("skip", 16, 8, 1, 1024, [W.decode_spec([50, 300, 129, 7])], seed=35,
+                        device="cuda")
+    host = HostInputs(step)
+    part = step.parts[0]
+    bad = step.out_loc.copy()
+    bad[1] = step.num_slots + 5
+    announce("decode+store with one out-of-pool slot")
+    out = host_u16(gpu_decode_store(step, part, out_loc=bad))
+    torch.cuda.synchronize()
+    kp, vp = host_u16(step.k_pool), host_u16(step.v_pool)
+    keep = np.ones(step.num_slots, bool)
+    keep[step.out_loc[1]] = False
+    assert np.array_equal(kp[keep], host.k_pool[keep])
+    assert np.array_equal(vp[keep], host.v_pool[keep])
+    assert np.array_equal(kp[step.out_loc[1]], host.k_pool0[step.out_loc[1]])  # untouched
+    ok = [0, 2, 3]
+    ref = oracle.decode_ref(host.q[0][ok], host.k_pool, host.v_pool, part.page_table[ok],
+                            part.seq_lens[ok], step.page_size, step.scale)
+    assert_close(out[ok], ref, "decode+store, the requests with valid slots")
+
+
+def test_decode_store_equals_store_then_decode():
+    """The fused call and store_kv followed by decode give the same pools bit for bit
+    and outputs within rounding order (the same kernels' arithmetic: identical here)."""
+    a = W.decode_b256(device="cuda", batch=64)
+    b = W.decode_b256(device="cuda", batch=64)
+    announce("decode+store vs store then decode (64 requests)")
+    out_a = host_u16(gpu_decode_store(a, a.parts[0]))
+    gpu_store(b)
+    out_b = host_u16(gpu_part(b, b.parts[0]))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(a.k_pool), host_u16(b.k_pool))
+    assert np.array_equal(host_u16(a.v_pool), host_u16(b.v_pool))
+    assert np.array_equal(out_a, out_b)
 
 
 def test_decode_gqa_constant_v():
