@@ -539,13 +539,38 @@ __device__ __forceinline__ int32_t group_of(int32_t x, int32_t nb_head, int32_t 
   return (int32_t)((((int64_t)x + 1) * groups + nb_head - 1) / nb_head) - 1;
 }
 
-// One wavefront per (request, q head) of a pair split between wavefronts w0 .. w1,
-// four per workgroup: split i comes from wavefront w0 + i, in slot 2w (that
-// wavefront's first segment) except for w0 when its range began before the pair
-// (slot 2w0 + 1). Lane l combines d = 2l, 2l+1. Up to 16 splits (the usual case) are
-// merged with one round of loads: lane s loads split s's log2-sum-exp while every lane
-// loads its part of all splits' outputs; longer rows go through a loop of 64 splits
-// at a time.
+// Merge of up to K splits with one round of loads: lane s loads split s's
+// log2-sum-exp while every lane loads its part (d = 2l, 2l+1) of all splits' outputs.
+template <int K, typename RowOf>
+__device__ __forceinline__ void merge_one_round(const float* __restrict__ part_o,
+                                                const float* __restrict__ part_lse,
+                                                const RowOf& row_of, int nsplit, int lane,
+                                                uint32_t* dst) {
+  const float lse_l = lane < nsplit ? part_lse[row_of(lane)] : kNegInf;
+  float2 v[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    v[i] = i < nsplit ? *(const float2*)(part_o + row_of(i) * kHeadDim + 2 * lane)
+                      : float2{0.f, 0.f};
+  const float mx = wave_max(lse_l);
+  const float w_l = lane < nsplit ? fast_exp2(lse_l - mx) : 0.f;
+  const float inv = 1.f / wave_sum(w_l);
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const float w = __shfl(w_l, i);  // 0 past nsplit
+    acc0 += w * v[i].x;
+    acc1 += w * v[i].y;
+  }
+  dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
+}
+
+// One wavefront per (request, q head) of a pair (b, g) split between the ranges of
+// groups c0 .. c1, four per workgroup: split i comes from wavefront w = (c0 + i) * Hkv
+// + g, in slot 2w (that wavefront's first segment) except for i = 0 when its range
+// began before the pair (slot 2w + 1). Lane l combines d = 2l, 2l+1. Up to 32 splits
+// (the usual case) are merged with one round of loads; longer rows go through a loop
+// of 64 splits at a time.
 constexpr int kMergeWaves = 4;
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -578,23 +603,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
   };
   uint32_t* dst = (uint32_t*)(out + ((int64_t)b * num_q_heads + h) * kHeadDim);
   if (nsplit <= 16) {
-    const float lse_l = lane < nsplit ? part_lse[row_of(lane)] : kNegInf;
-    float2 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = i < nsplit ? *(const float2*)(part_o + row_of(i) * kHeadDim + 2 * lane)
-                        : float2{0.f, 0.f};
-    const float mx = wave_max(lse_l);
-    const float w_l = lane < nsplit ? fast_exp2(lse_l - mx) : 0.f;
-    const float inv = 1.f / wave_sum(w_l);
-    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float w = __shfl(w_l, i);  // 0 past nsplit
-      acc0 += w * v[i].x;
-      acc1 += w * v[i].y;
-    }
-    dst[lane] = pack_bf16x2(acc0 * inv, acc1 * inv);
+    merge_one_round<16>(part_o, part_lse, row_of, nsplit, lane, dst);
+    return;
+  }
+  if (nsplit <= 32) {
+    merge_one_round<32>(part_o, part_lse, row_of, nsplit, lane, dst);
     return;
   }
   float mx = kNegInf;
