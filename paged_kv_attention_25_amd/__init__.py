@@ -31,7 +31,8 @@ PKA_E_UNSUPPORTED = -3
 PKA_E_WORKSPACE = -4
 PKA_E_HIP = -5
 
-# Every symbol include/pka.h declares.
+# Every symbol include/pka.h and include/pka_sched.h declare (the latter bound in
+# the `sched` submodule).
 EXPORTED_SYMBOLS = (
     "pka_version",
     "pka_status_string",
@@ -41,6 +42,15 @@ EXPORTED_SYMBOLS = (
     "pka_decode_workspace_bytes",
     "pka_paged_attn_prefill",
     "pka_prefill_workspace_bytes",
+    "pka_sched_create",
+    "pka_sched_destroy",
+    "pka_sched_add_request",
+    "pka_sched_prefill_batch",
+    "pka_sched_push_token",
+    "pka_sched_decode_batch",
+    "pka_sched_finish",
+    "pka_sched_request_pages",
+    "pka_sched_get_stats",
 )
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/pka.h"
+#include "../../include/pka_sched.h"
 #include "pka_kernels.h"
 
 namespace {
@@ -43,6 +44,9 @@ const char* pka_status_string(int status) {
     case PKA_E_UNSUPPORTED: return "unsupported by these kernels";
     case PKA_E_WORKSPACE: return "workspace missing or too small";
     case PKA_E_HIP: return "HIP runtime error";
+    case PKA_E_STATE: return "unknown request or wrong request state";
+    case PKA_E_CAPACITY: return "output array or page-table row too small";
+    case PKA_E_NOMEM: return "host memory allocation failed";
     default: return "unknown status";
   }
 }

@@ -14,7 +14,7 @@ import pytest
 import paged_kv_attention_25_amd as pka
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pka.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pka.h", "pka_sched.h")]
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below returns first
 
 
@@ -27,7 +27,7 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pka_\w+)\s*\(", text)))
 

@@ -1,0 +1,375 @@
+"""Host-side metadata producer (page allocator, prefix cache, batch builder): the
+oracle pinned to a hand-worked scenario and to a closed form, then the library
+(csrc/sched.cpp through its C ABI) against the oracle on random request streams,
+bit-exact on every unique result, with a slot-content model that checks every page
+the produced metadata points attention at.
+
+CPU only.
+"""
+import os
+import random
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_25_amd as pka
+from oracle.prefix_cache_ref import PrefixCacheRef, longest_cached_prefix_bruteforce
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "prefix_cache_scenario.txt")
+STAT_KEYS = ("free_pages", "cached_pages", "locked_pages", "private_pages", "evicted_pages")
+
+
+@pytest.fixture(scope="module")
+def sched_mod():
+    if not os.path.exists(pka.LIB_PATH):
+        from paged_kv_attention_25_amd.build import build_library
+        build_library()
+    from paged_kv_attention_25_amd import sched
+    return sched
+
+
+def read_scenario():
+    cfg, steps = None, []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("config"):
+            p, n, pol, budget = line.split()[1:]
+            cfg = (int(p), int(n), pol, int(budget))
+            continue
+        op, rows, stats = (x.strip() for x in line.split(";"))
+        want_rows = [] if rows == "-" else [
+            (r.split(":")[0], int(r.split(":")[1]), int(r.split(":")[2])) for r in rows.split(",")]
+        steps.append((op.split(), want_rows, tuple(int(x) for x in stats.split())))
+    return cfg, steps
+
+
+def run_scenario_on_oracle(ref, steps, names):
+    for words, want_rows, want_stats in steps:
+        rows = apply_oracle(ref, words, names)
+        got_rows = [(names[r], p, e) for r, p, e in rows]
+        st = ref.stats()
+        yield words, got_rows, want_rows, tuple(st[k] for k in STAT_KEYS), want_stats
+
+
+def apply_oracle(ref, words, names):
+    op = words[0]
+    if op == "add":
+        rid = len(names)
+        names[rid] = words[1]
+        names[words[1]] = rid
+        ref.add_request(rid, [int(x) for x in words[2:]])
+        return []
+    if op == "prefill":
+        return ref.prefill_batch(1 << 30, 1 << 30)
+    if op == "decode":
+        return ref.decode_batch(1 << 30, 1 << 30)
+    if op == "push":
+        ref.push_token(names[words[1]], int(words[2]))
+        return []
+    if op == "finish":
+        ref.finish(names[words[1]])
+        return []
+    raise ValueError(op)
+
+
+# --- the oracle against its pins -------------------------------------------------------
+
+
+def test_oracle_hand_worked_scenario():
+    (P, n, pol, budget), steps = read_scenario()
+    ref = PrefixCacheRef(P, n, pol, budget)
+    for words, got, want, got_st, want_st in run_scenario_on_oracle(ref, steps, {}):
+        assert got == want, words
+        assert got_st == want_st, words
+
+
+@pytest.mark.parametrize("P", [1, 2, 5])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_oracle_match_equals_closed_form_without_eviction(P, seed):
+    # With a pool that never runs out nothing is evicted, so the match on admission is
+    # the longest whole-page common prefix (capped below the prompt's last token) with
+    # the stored part of any finished request.
+    rng = random.Random(seed)
+    docs = [[rng.randrange(4) for _ in range(rng.randrange(0, 25))] for _ in range(4)]
+    ref = PrefixCacheRef(P, 10 ** 6, "radix", 10 ** 6)
+    history = []
+    for rid in range(60):
+        toks = rng.choice(docs) + [rng.randrange(4) for _ in range(rng.randrange(1, 12))]
+        ref.add_request(rid, toks)
+        rows = ref.prefill_batch(1 << 30, 1 << 30)
+        assert [(r, p) for r, p, _ in rows] == [(rid, longest_cached_prefix_bruteforce(toks, history, P))]
+        for _ in range(rng.randrange(0, 4)):
+            ref.push_token(rid, rng.randrange(4))
+            ref.decode_batch(1 << 30, 1 << 30)
+        stored = ref.reqs[rid]["tokens"][:ref.reqs[rid]["cached"]]
+        ref.finish(rid)
+        history.append(stored)
+
+
+class _EvictNewest(PrefixCacheRef):
+    """Planted mistake: evicts the most recently used leaf."""
+
+    def _alloc(self):
+        if self.free > 0:
+            self.free -= 1
+            return True
+        cands = [k for k, (_, locks) in self.cache.items() if locks == 0 and self._is_leaf(k)]
+        if not cands:
+            return False
+        del self.cache[max(cands, key=lambda k: self.cache[k][0])]
+        self.evicted += 1
+        return True
+
+
+class _NoMatchCap(PrefixCacheRef):
+    """Planted mistake: a fully cached prompt is matched whole (nothing left to compute)."""
+
+    def _admit(self, r):
+        n = r["n_prompt"]
+        r["n_prompt"] = n + 1
+        super()._admit(r)
+        r["n_prompt"] = n
+
+
+class _EvictLocked(PrefixCacheRef):
+    """Planted mistake: ignores the locks of live requests when evicting."""
+
+    def _alloc(self):
+        if self.free > 0:
+            self.free -= 1
+            return True
+        cands = [k for k in self.cache if self._is_leaf(k)]
+        if not cands:
+            return False
+        del self.cache[min(cands, key=lambda k: self.cache[k][0])]
+        self.evicted += 1
+        return True
+
+
+@pytest.mark.parametrize("planted", [_EvictNewest, _EvictLocked])
+def test_planted_eviction_mistakes_fail_the_scenario(planted):
+    (P, n, pol, budget), steps = read_scenario()
+    ref = planted(P, n, pol, budget)
+    ok = True
+    try:
+        for _, got, want, got_st, want_st in run_scenario_on_oracle(ref, steps, {}):
+            ok = ok and got == want and got_st == want_st
+    except (AssertionError, KeyError, ValueError):
+        ok = False
+    assert not ok
+
+
+def test_planted_missing_cap_fails_the_closed_form():
+    ref = _NoMatchCap(2, 1000, "radix", 1000)
+    ref.add_request(0, [1, 2, 3, 4])
+    ref.prefill_batch(10, 10)
+    stored = ref.reqs[0]["tokens"][:ref.reqs[0]["cached"]]
+    ref.finish(0)
+    ref.add_request(1, [1, 2, 3, 4])
+    rows = ref.prefill_batch(10, 10)
+    closed = longest_cached_prefix_bruteforce([1, 2, 3, 4], [stored], 2)
+    assert [(r, p) for r, p, _ in rows] != [(1, closed)]
+
+
+# --- the library against the oracle ----------------------------------------------------
+
+
+def test_library_hand_worked_scenario(sched_mod):
+    (P, n, pol, budget), steps = read_scenario()
+    s = sched_mod.Scheduler(P, n, pol, budget, max_batch=16, table_width=16, max_tokens=1000)
+    names = {}
+    for words, want_rows, want_stats in steps:
+        op = words[0]
+        rows = []
+        if op == "add":
+            rid = len(names)
+            names[rid] = words[1]
+            names[words[1]] = rid
+            s.add_request(rid, [int(x) for x in words[2:]])
+        elif op in ("prefill", "decode"):
+            b = s.prefill_batch() if op == "prefill" else s.decode_batch()
+            rows = [(names[int(r)], int(p), int(e))
+                    for r, p, e in zip(b.req_ids, b.prefix_lens, b.extend_lens)]
+        elif op == "push":
+            s.push_token(names[words[1]], int(words[2]))
+        elif op == "finish":
+            s.finish(names[words[1]])
+        st = s.stats()
+        assert rows == want_rows, words
+        assert tuple(st[k] for k in STAT_KEYS) == want_stats, words
+
+
+class SlotModel:
+    """Which token prefix each pool slot holds, from the out_loc writes of every batch."""
+
+    def __init__(self, P, num_pages):
+        self.P, self.num_pages, self.slot = P, num_pages, {}
+
+    def apply(self, b, tokens_of):
+        P = self.P
+        assert b.cu_extend[0] == 0 and np.all(np.diff(b.cu_extend) == b.extend_lens)
+        assert np.array_equal(b.seq_lens, b.prefix_lens + b.extend_lens)
+        assert b.num_tokens == int(b.extend_lens.sum()) == b.out_loc.size
+        assert len(set(b.out_loc.tolist())) == b.out_loc.size  # distinct slots
+        if b.batch:
+            assert b.max_extend == int(b.extend_lens.max())
+            assert b.max_seq_len == int(b.seq_lens.max())
+        for i in range(b.batch):
+            rid, pre, ext, seq = (int(b.req_ids[i]), int(b.prefix_lens[i]), int(b.extend_lens[i]),
+                                  int(b.seq_lens[i]))
+            toks = tokens_of[rid]
+            row = b.page_table[i]
+            used = -(-seq // P)
+            assert np.all((row[:used] >= 0) & (row[:used] < self.num_pages))
+            assert len(set(row[:used].tolist())) == used
+            assert np.all(row[used:] == 0)
+            for j in range(ext):
+                pos = pre + j
+                slot = int(b.out_loc[b.cu_extend[i] + j])
+                assert slot == int(row[pos // P]) * P + pos % P
+                self.slot[slot] = tuple(toks[:pos + 1])
+        for i in range(b.batch):
+            self.check_row(b.page_table[i], int(b.seq_lens[i]), tokens_of[int(b.req_ids[i])])
+
+    def check_row(self, pages, n, toks):
+        P = self.P
+        for j in range(n):
+            assert self.slot.get(int(pages[j // P]) * P + j % P) == tuple(toks[:j + 1]), j
+
+
+def drive(sched_mod, P, num_pages, policy, budget, max_batch, seed, steps=500):
+    rng = random.Random(seed)
+    width = 512
+    s = sched_mod.Scheduler(P, num_pages, policy, budget, max_batch=max_batch, table_width=width,
+                            max_tokens=budget)
+    ref = PrefixCacheRef(P, num_pages, policy, budget)
+    model = SlotModel(P, num_pages)
+    docs = [[rng.randrange(3) for _ in range(rng.randrange(0, 40))] for _ in range(5)]
+    tokens_of, live, next_id, started = {}, [], 0, set()
+    counts = dict(prefill_rows=0, decode_rows=0, evicted=0, reused=0)
+    for _ in range(steps):
+        op = rng.random()
+        if op < 0.25 and len(live) < 12:
+            toks = rng.choice(docs) + [rng.randrange(3) for _ in range(rng.randrange(1, 30))]
+            s.add_request(next_id, toks)
+            ref.add_request(next_id, toks)
+            tokens_of[next_id] = list(toks)
+            live.append(next_id)
+            next_id += 1
+        elif op < 0.5:
+            b = s.prefill_batch()
+            rows = ref.prefill_batch(max_batch, budget)
+            assert [(int(r), int(p), int(e)) for r, p, e in
+                    zip(b.req_ids, b.prefix_lens, b.extend_lens)] == rows
+            model.apply(b, tokens_of)
+            counts["prefill_rows"] += b.batch
+            # reuse: the prefix of a request's first chunk (later chunks extend its own)
+            counts["reused"] += sum(p for r, p, _ in rows if r not in started)
+            started.update(r for r, _, _ in rows)
+        elif op < 0.65:
+            for rid in live:
+                r = ref.reqs[rid]
+                if r["state"] == "running" and not r["pending"] and rng.random() < 0.8:
+                    t = rng.randrange(3)
+                    s.push_token(rid, t)
+                    ref.push_token(rid, t)
+                    tokens_of[rid].append(t)
+        elif op < 0.85:
+            b = s.decode_batch()
+            rows = ref.decode_batch(max_batch, budget)
+            assert [(int(r), int(p), int(e)) for r, p, e in
+                    zip(b.req_ids, b.prefix_lens, b.extend_lens)] == rows
+            model.apply(b, tokens_of)
+            counts["decode_rows"] += b.batch
+        elif live:
+            rid = live.pop(rng.randrange(len(live)))
+            s.finish(rid)
+            ref.finish(rid)
+        st, want = s.stats(), ref.stats()
+        assert st == want
+        # every live request's stored tokens still sit in the slots its pages name
+        for rid in live:
+            pages, cached = s.request_pages(rid)
+            assert cached == ref.reqs[rid]["cached"]
+            assert pages.size == ref.reqs[rid]["pages"]
+            model.check_row(pages, cached, tokens_of[rid])
+    counts["evicted"] = s.stats()["evicted_pages"]
+    s.close()
+    return counts
+
+
+@pytest.mark.parametrize("policy", ["radix", "naive"])
+@pytest.mark.parametrize("P,num_pages", [(1, 200), (3, 60), (16, 12)])
+@pytest.mark.parametrize("budget,max_batch", [(7, 4), (64, 16)])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_library_matches_oracle_on_random_streams(sched_mod, policy, P, num_pages, budget,
+                                                  max_batch, seed):
+    counts = drive(sched_mod, P, num_pages, policy, budget, max_batch, seed)
+    assert counts["prefill_rows"] > 0 and counts["decode_rows"] > 0
+    if policy == "naive":
+        assert counts["reused"] == 0 and counts["evicted"] == 0
+
+
+def test_random_streams_exercise_reuse_and_eviction(sched_mod):
+    # the streams above are not vacuous: radix runs reuse prefixes and evict
+    total = dict(reused=0, evicted=0)
+    for seed in range(3):
+        c = drive(sched_mod, 1, 200, "radix", 64, 16, seed)
+        total["reused"] += c["reused"]
+        total["evicted"] += c["evicted"]
+    assert total["reused"] > 1000 and total["evicted"] > 1000
+
+
+def test_chunked_prefill_budget_8192(sched_mod):
+    # one 20000-token prompt in 8192-token chunks; a second request joins the batch
+    # that has budget left.
+    s = sched_mod.Scheduler(16, 4096, "radix", 8192, max_batch=8, table_width=2048)
+    s.add_request(1, np.arange(20000) % 1000)
+    s.add_request(2, np.arange(100) + 5000)
+    ext = []
+    for _ in range(3):
+        b = s.prefill_batch()
+        ext.append([(int(r), int(p), int(e)) for r, p, e in zip(b.req_ids, b.prefix_lens,
+                                                                 b.extend_lens)])
+    assert ext == [[(1, 0, 8192)], [(1, 8192, 8192)], [(1, 16384, 3616), (2, 0, 100)]]
+
+
+def test_errors(sched_mod):
+    S = sched_mod.Scheduler
+    with pytest.raises(pka.PkaError) as e:
+        S(0, 10)
+    assert e.value.status == pka.PKA_E_SHAPE
+    with pytest.raises(pka.PkaError):
+        S(1, 10, max_prefill_tokens=0)
+    s = S(4, 16, "radix", 64, max_batch=4, table_width=2)
+    s.add_request(1, [1, 2, 3])
+    with pytest.raises(pka.PkaError) as e:
+        s.add_request(1, [4])
+    assert e.value.status == sched_mod.PKA_E_STATE
+    with pytest.raises(pka.PkaError) as e:
+        s.add_request(2, [])
+    assert e.value.status == pka.PKA_E_SHAPE
+    with pytest.raises(pka.PkaError) as e:
+        s.push_token(1, 5)            # not running yet
+    assert e.value.status == sched_mod.PKA_E_STATE
+    with pytest.raises(pka.PkaError) as e:
+        s.finish(99)
+    assert e.value.status == sched_mod.PKA_E_STATE
+    s.add_request(3, list(range(9)))  # 3 pages > table_width 2
+    before = s.stats()
+    with pytest.raises(pka.PkaError) as e:
+        s.prefill_batch()
+    assert e.value.status == sched_mod.PKA_E_CAPACITY
+    assert s.stats() == before
+    s.finish(3)
+    b = s.prefill_batch()
+    assert b.batch == 1 and b.num_tokens == 3
+    s.push_token(1, 7)
+    with pytest.raises(pka.PkaError) as e:
+        s.push_token(1, 8)            # already pending
+    assert e.value.status == sched_mod.PKA_E_STATE
+    for code in (-6, -7, -8):
+        assert pka.status_string(code) != "unknown status"
