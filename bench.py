@@ -395,6 +395,97 @@ def time_part(name, steps, warmup, flush, log):
     return rec
 
 
+def host_sched_bench(log, decode_steps=20):
+    """Host-side metadata producer (csrc/sched.cpp) on the decode_b256 request mix: 256
+    prompts, lengths U[200, 2048], all starting with one 128-token system prompt, page
+    size 1, a 2^20-page pool, radix cache, 8192-token prefill batches. Times (host
+    µs, C calls made directly on preallocated buffers): the prefill batches that take
+    every prompt in, a decode step (256 pushed tokens + the decode batch), finishing
+    every request (its pages join the cache), and admitting 256 new requests of the same
+    mix against that cache (prefix matches). The oracle (oracle/prefix_cache_ref.py)
+    runs the prefill and decode part of the same stream beside it."""
+    import ctypes
+    from paged_kv_attention_25_amd import sched as S
+    from oracle.prefix_cache_ref import PrefixCacheRef
+    rng = np.random.default_rng(2)
+    B, W = 256, 2048 + decode_steps + 1
+    system = rng.integers(0, 32000, 128)
+
+    def prompts():
+        return [np.concatenate([system, rng.integers(0, 32000, int(n) - 128)]).astype(np.int32)
+                for n in rng.integers(200, 2049, B)]
+
+    first, second = prompts(), prompts()
+    nxt = rng.integers(0, 32000, (decode_steps, B)).astype(np.int32)
+    s = S.Scheduler(1, 1 << 20, "radix", 8192, max_batch=B, table_width=W, max_tokens=8192)
+    L, h, bufs = s._L, s._h, s._bufs
+    for a in bufs.values():   # fault the output buffers in before timing
+        a.fill(1)
+    c = S._Batch(B, W, 8192, 0, *(bufs[k].ctypes.data for k in (
+        "req_ids", "page_table", "seq_lens", "prefix_lens", "extend_lens", "cu_extend",
+        "out_loc")), 0, 0, 0, 0)
+    ids = np.arange(B, dtype=np.int64)
+    tc = time.perf_counter
+
+    def prefill_all(offset, reqs):
+        t0 = tc()
+        for i, p in enumerate(reqs):
+            L.pka_sched_add_request(h, offset + i, p.ctypes.data, int(p.size))
+        t1 = tc()
+        nb, reused = 0, 0
+        while True:
+            assert L.pka_sched_prefill_batch(h, ctypes.byref(c)) == 0
+            if c.batch == 0:
+                break
+            nb += 1
+        return (t1 - t0) * 1e6 / B, (tc() - t1) * 1e6, nb
+
+    add_us, pre_us, n_pre = prefill_all(0, first)
+    t0 = tc()
+    entries = 0
+    for k in range(decode_steps):
+        assert L.pka_sched_push_tokens(h, ids.ctypes.data, nxt[k].ctypes.data, B) == 0
+        assert L.pka_sched_decode_batch(h, ctypes.byref(c)) == 0 and c.batch == B
+        entries += int(bufs["seq_lens"][:B].sum())
+    dec_us = (tc() - t0) * 1e6 / decode_steps
+    t0 = tc()
+    for i in range(B):
+        assert L.pka_sched_finish(h, i) == 0
+    fin_us = (tc() - t0) * 1e6 / B
+    add2_us, pre2_us, n_pre2 = prefill_all(B, second)
+    st = s.stats()
+    s.close()
+
+    ref = PrefixCacheRef(1, 1 << 20, "radix", 8192)
+    t0 = tc()
+    for i, p in enumerate(first):
+        ref.add_request(i, p.tolist())
+    while ref.prefill_batch(B, 8192):
+        pass
+    t1 = tc()
+    for k in range(decode_steps):
+        for i in range(B):
+            ref.push_token(i, int(nxt[k, i]))
+        ref.decode_batch(B, 8192)
+    t2 = tc()
+    rec = {"workload": "decode_b256 request mix: 256 prompts U[200,2048] sharing a 128-token "
+                       "system prompt, page_size 1, 2^20 pages, radix, 8192-token chunks",
+           "prefill_batches": n_pre, "prefill_all_us": round(pre_us, 1),
+           "prefill_us_per_batch": round(pre_us / n_pre, 1),
+           "add_request_us": round(add_us, 2),
+           "decode_step_us": round(dec_us, 1),
+           "decode_step_page_table_entries": entries // decode_steps,
+           "finish_us_per_request": round(fin_us, 2),
+           "second_wave": {"prefill_all_us": round(pre2_us, 1), "prefill_batches": n_pre2,
+                           "cached_pages": st["cached_pages"], "locked_pages": st["locked_pages"]},
+           "oracle": {"prefill_all_us": round((t1 - t0) * 1e6, 1),
+                      "decode_step_us": round((t2 - t1) * 1e6 / decode_steps, 1),
+                      "note": "counts pages only: builds no page table"},
+           "unit": "host us"}
+    log(f"host_sched: {rec}")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -510,6 +601,7 @@ def main():
     if not args.quick:
         for name in PART_NAMES:
             parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log)
+        parts["host_sched"] = host_sched_bench(log)
         cp = parts["chunked_prefill"]
         result["prefill"] = {"workload": "chunked_prefill: Qwen3-14B heads 40q/8kv, 32 requests, "
                                          "prefixes U[0,4096], 8192 new tokens, page_size 16",

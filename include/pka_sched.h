@@ -66,7 +66,8 @@ typedef struct pka_sched pka_sched; /* opaque */
  * pointers (host memory); the call fills the arrays and the four counts.
  *   req_ids      [max_batch]               request id of row b
  *   page_table   [max_batch * table_width] page ids, row b = request b; entries past
- *                                          ceil(seq_lens[b] / page_size) are 0
+ *                                          ceil(seq_lens[b] / page_size) are not written
+ *                                          (no attention call reads them)
  *   seq_lens, prefix_lens, extend_lens  [max_batch]
  *   cu_extend    [max_batch + 1]           exclusive prefix sums of extend_lens
  *   out_loc      [max_tokens]              slot of every new token, rows in order
@@ -128,6 +129,12 @@ int pka_sched_prefill_batch(pka_sched* s, pka_batch* out);
  * sampled from its last output. PKA_E_STATE if the request is not running or already
  * has a pending token. */
 int pka_sched_push_token(pka_sched* s, int64_t req_id, int32_t token);
+
+/* pka_sched_push_token for n requests at once (one call per decode step): request
+ * req_ids[i] gets tokens[i]. All or nothing: PKA_E_STATE (and no change) if any id is
+ * unknown, not running, already pending or listed twice. */
+int pka_sched_push_tokens(pka_sched* s, const int64_t* req_ids, const int32_t* tokens,
+                          int32_t n);
 
 /* Build the next decode batch: every running request with a pending token, in the
  * order their prompts completed, each getting the slot of its new token (a new page

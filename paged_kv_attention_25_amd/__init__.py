@@ -47,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "pka_sched_add_request",
     "pka_sched_prefill_batch",
     "pka_sched_push_token",
+    "pka_sched_push_tokens",
     "pka_sched_decode_batch",
     "pka_sched_finish",
     "pka_sched_request_pages",

@@ -292,7 +292,7 @@ struct pka_sched {
     out->cu_extend[b] = t0;
     int32_t* row = out->page_table + (int64_t)b * out->table_width;
     const int32_t used = (int32_t)ceil_div(seq, P);
-    for (int32_t k = 0; k < out->table_width; ++k) row[k] = k < used ? r->pages[k] : 0;
+    std::copy(r->pages.begin(), r->pages.begin() + used, row);
     for (int32_t i = 0; i < extend; ++i) {
       const int32_t pos = r->cached + i;
       out->out_loc[t0 + i] = r->pages[pos / P] * P + pos % P;
@@ -423,6 +423,30 @@ int pka_sched_push_token(pka_sched* s, int64_t req_id, int32_t token) {
     if (r->state != State::kRunning || r->pending) return PKA_E_STATE;
     r->tokens.push_back(token);
     r->pending = true;
+    return PKA_OK;
+  });
+}
+
+int pka_sched_push_tokens(pka_sched* s, const int64_t* req_ids, const int32_t* tokens,
+                          int32_t n) {
+  return guarded([&]() -> int {
+    if (s == nullptr) return PKA_E_NULLPTR;
+    if (n < 0) return PKA_E_SHAPE;
+    if (n > 0 && (req_ids == nullptr || tokens == nullptr)) return PKA_E_NULLPTR;
+    // Mark each request pending as it is checked (a second occurrence then fails the
+    // check); on any failure the marks made so far are undone.
+    std::vector<Request*> rs((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = s->reqs.find(req_ids[i]);
+      Request* r = it == s->reqs.end() ? nullptr : it->second.get();
+      if (r == nullptr || r->state != State::kRunning || r->pending) {
+        for (int32_t k = 0; k < i; ++k) rs[(size_t)k]->pending = false;
+        return PKA_E_STATE;
+      }
+      r->pending = true;
+      rs[(size_t)i] = r;
+    }
+    for (int32_t i = 0; i < n; ++i) rs[(size_t)i]->tokens.push_back(tokens[i]);
     return PKA_OK;
   });
 }

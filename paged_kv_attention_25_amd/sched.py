@@ -33,6 +33,7 @@ SCHED_SYMBOLS = (
     "pka_sched_add_request",
     "pka_sched_prefill_batch",
     "pka_sched_push_token",
+    "pka_sched_push_tokens",
     "pka_sched_decode_batch",
     "pka_sched_finish",
     "pka_sched_request_pages",
@@ -92,6 +93,8 @@ def _lib():
         L.pka_sched_prefill_batch.argtypes = [vp, ctypes.POINTER(_Batch)]
         L.pka_sched_push_token.restype = ctypes.c_int
         L.pka_sched_push_token.argtypes = [vp, i64, i32]
+        L.pka_sched_push_tokens.restype = ctypes.c_int
+        L.pka_sched_push_tokens.argtypes = [vp, vp, vp, i32]
         L.pka_sched_decode_batch.restype = ctypes.c_int
         L.pka_sched_decode_batch.argtypes = [vp, ctypes.POINTER(_Batch)]
         L.pka_sched_finish.restype = ctypes.c_int
@@ -195,6 +198,13 @@ class Scheduler:
     def push_token(self, req_id: int, token: int):
         _check(self._L.pka_sched_push_token(self._h, int(req_id), int(token)),
                "pka_sched_push_token")
+
+    def push_tokens(self, req_ids, tokens):
+        ids = np.ascontiguousarray(req_ids, dtype=np.int64)
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        assert ids.shape == tok.shape and ids.ndim == 1
+        _check(self._L.pka_sched_push_tokens(self._h, ids.ctypes.data, tok.ctypes.data,
+                                             int(ids.size)), "pka_sched_push_tokens")
 
     def finish(self, req_id: int):
         _check(self._L.pka_sched_finish(self._h, int(req_id)), "pka_sched_finish")

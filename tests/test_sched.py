@@ -225,7 +225,6 @@ class SlotModel:
             used = -(-seq // P)
             assert np.all((row[:used] >= 0) & (row[:used] < self.num_pages))
             assert len(set(row[:used].tolist())) == used
-            assert np.all(row[used:] == 0)
             for j in range(ext):
                 pos = pre + j
                 slot = int(b.out_loc[b.cu_extend[i] + j])
@@ -270,13 +269,20 @@ def drive(sched_mod, P, num_pages, policy, budget, max_batch, seed, steps=500):
             counts["reused"] += sum(p for r, p, _ in rows if r not in started)
             started.update(r for r, _, _ in rows)
         elif op < 0.65:
+            ids, toks = [], []
             for rid in live:
                 r = ref.reqs[rid]
                 if r["state"] == "running" and not r["pending"] and rng.random() < 0.8:
                     t = rng.randrange(3)
-                    s.push_token(rid, t)
+                    ids.append(rid)
+                    toks.append(t)
                     ref.push_token(rid, t)
                     tokens_of[rid].append(t)
+            if rng.random() < 0.5:
+                s.push_tokens(ids, toks)
+            else:
+                for rid, t in zip(ids, toks):
+                    s.push_token(rid, t)
         elif op < 0.85:
             b = s.decode_batch()
             rows = ref.decode_batch(max_batch, budget)
@@ -371,5 +377,18 @@ def test_errors(sched_mod):
     with pytest.raises(pka.PkaError) as e:
         s.push_token(1, 8)            # already pending
     assert e.value.status == sched_mod.PKA_E_STATE
+    # batched push: all or nothing
+    s.finish(1)
+    s.add_request(4, [1])
+    s.add_request(5, [2])
+    b = s.prefill_batch()
+    assert sorted(b.req_ids.tolist()) == [4, 5]
+    for bad in ([4, 4], [4, 99], [4, 6]):
+        with pytest.raises(pka.PkaError) as e:
+            s.push_tokens(bad, [1, 1])
+        assert e.value.status == sched_mod.PKA_E_STATE
+    s.push_tokens([4, 5], [8, 9])     # the failed calls left no token pending
+    b = s.decode_batch()
+    assert b.req_ids.tolist() == [4, 5] and b.prefix_lens.tolist() == [1, 1]
     for code in (-6, -7, -8):
         assert pka.status_string(code) != "unknown status"
