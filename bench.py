@@ -395,6 +395,41 @@ def time_part(name, steps, warmup, flush, log):
     return rec
 
 
+PAGE_SIZES = (1, 16, 32, 64)
+
+
+def page_size_sweep(steps, warmup, flush, log):
+    """decode_b256 (the decode_store step) and chunked_prefill with the pool cut into
+    pages of 1, 16, 32 and 64 slots: the same requests, pages drawn at random. The
+    kernels take any page size at run time (powers of two by shift and mask)."""
+    import torch
+    from paged_kv_attention_25_amd import workloads as W
+    out = {"decode_b256": {}, "chunked_prefill": {}}
+    for P in PAGE_SIZES:
+        st = W.decode_b256(device="cuda", fill="zero", page_size=P)
+        r = Runner(st, fused=True)
+        torch.cuda.synchronize()
+        _, tot, _ = time_step(r, steps, warmup, flush)
+        nbytes = decode_bytes(st.parts[0], st) + store_bytes(st)
+        out["decode_b256"][f"P{P}"] = {"step_us": round(tot * 1e3, 2),
+                                       "GBs": round(nbytes / (tot * 1e-3) / 1e9, 1)}
+        del r, st
+        torch.cuda.empty_cache()
+    for P in PAGE_SIZES:
+        st = W.chunked_prefill(device="cuda", fill="zero", page_size=P)
+        r = Runner(st)
+        torch.cuda.synchronize()
+        seg, _, _ = time_step(r, steps, max(warmup, PART_WARMUP), flush)
+        us = seg[1] * 1e3
+        tf = prefill_flops(st.parts[0], st) / (us * 1e-6) / 1e12
+        out["chunked_prefill"][f"P{P}"] = {"prefill_us": round(us, 2),
+                                           "TFLOPs": round(tf, 1)}
+        del r, st
+        torch.cuda.empty_cache()
+    log(f"page sizes: {out}")
+    return out
+
+
 def host_sched_bench(log, decode_steps=20):
     """Host-side metadata producer (csrc/sched.cpp) on the decode_b256 request mix: 256
     prompts, lengths U[200, 2048], all starting with one 128-token system prompt, page
@@ -602,6 +637,7 @@ def main():
         for name in PART_NAMES:
             parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log)
         parts["host_sched"] = host_sched_bench(log)
+        parts["page_sizes"] = page_size_sweep(args.steps, args.warmup, flush, log)
         cp = parts["chunked_prefill"]
         result["prefill"] = {"workload": "chunked_prefill: Qwen3-14B heads 40q/8kv, 32 requests, "
                                          "prefixes U[0,4096], 8192 new tokens, page_size 16",

@@ -198,20 +198,23 @@ def tiny_decode(seed=1, device="cpu", fill="nan"):
                       seed, device, fill)
 
 
-def decode_b256(seed=2, device="cpu", fill="nan", batch=256):
+def decode_b256(seed=2, device="cpu", fill="nan", batch=256, page_size=1):
+    """page_size other than 1: the same requests in a pool of 2^20 slots cut into pages
+    of that size, pages drawn at random."""
     rng = np.random.default_rng(seed + 1000)
     seq = rng.integers(200, 2048, size=batch, endpoint=True)
-    return build_step("decode_b256", 16, 8, 1, 1 << 20, [decode_spec(seq)], seed, device, fill)
+    return build_step("decode_b256", 16, 8, page_size, (1 << 20) // page_size,
+                      [decode_spec(seq)], seed, device, fill)
 
 
 def chunked_prefill(seed=3, device="cpu", fill="nan", requests=32, total_extend=8192,
-                    max_prefix=4096):
+                    max_prefix=4096, page_size=16):
     rng = np.random.default_rng(seed + 1000)
     prefix = rng.integers(0, max_prefix, size=requests, endpoint=True)
     extend = random_composition(rng, total_extend, requests)
     seq = prefix + extend
-    pages_needed = int((-(-seq // 16)).sum())
-    return build_step("chunked_prefill", 40, 8, 16, 2 * pages_needed,
+    pages_needed = int((-(-seq // page_size)).sum())
+    return build_step("chunked_prefill", 40, 8, page_size, 2 * pages_needed,
                       [("prefill", prefix, extend)], seed, device, fill)
 
 

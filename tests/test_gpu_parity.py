@@ -85,6 +85,13 @@ def test_decode_b256_full():
     run_decode_case(W.decode_b256(device="cuda"), "decode_b256 all requests")
 
 
+@pytest.mark.parametrize("P", [16, 32, 64])
+def test_decode_b256_page_sizes_sampled(P):
+    # the decode_b256 requests in a 2^20-slot pool cut into pages of P slots
+    step = W.decode_b256(device="cuda", page_size=P)
+    run_decode_case(step, f"decode_b256 P={P} (16 requests)", requests=list(range(3, 256, 16)))
+
+
 def test_decode_long_sampled():
     step = W.long_decode(device="cuda")
     run_decode_case(step, "long_decode 32x32768 P=64 (8 requests)", requests=[0, 5, 9, 13, 18,
@@ -379,6 +386,22 @@ def test_prefill_chunked_sampled():
             windows.append((b, max(40, eb - 40), eb))
     run_prefill_case(step, "chunked_prefill 32 req, 8192 tokens, P=16 (windows)",
                      windows=windows)
+
+
+@pytest.mark.parametrize("P", [1, 32, 64])
+def test_prefill_chunked_page_sizes_sampled(P):
+    # the chunked_prefill requests with the pool cut into other page sizes (the
+    # page-size sweep of the benchmark)
+    step = W.chunked_prefill(device="cuda", page_size=P)
+    part = step.parts[0]
+    e = part.extend_lens
+    windows = []
+    for b in sorted({int(np.argmax(e)), int(np.argmax(part.prefix_lens)), 0, 13, 31}):
+        eb = int(e[b])
+        windows.append((b, 0, min(eb, 32)))
+        if eb > 32:
+            windows.append((b, max(32, eb - 32), eb))
+    run_prefill_case(step, f"chunked_prefill P={P} (windows)", windows=windows)
 
 
 def test_prefill_tp4_chunk_sampled():
