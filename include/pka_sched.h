@@ -144,7 +144,10 @@ int pka_sched_push_tokens(pka_sched* s, const int64_t* req_ids, const int32_t* t
 int pka_sched_decode_batch(pka_sched* s, pka_batch* out);
 
 /* Retire a request in any state: its whole pages join the prefix cache (radix
- * policy) and its other pages return to the free list. */
+ * policy) and its other pages return to the free list. A batch counts its rows' new
+ * tokens as stored when it is built, so finish a request only after the store of the
+ * last batch that extended it has run (or been ordered before any later use of the
+ * pool on the same stream); otherwise the cache would hold pages never written. */
 int pka_sched_finish(pka_sched* s, int64_t req_id);
 
 /* Current page-table row of a live request: pages[0 .. *n_pages - 1] hold its

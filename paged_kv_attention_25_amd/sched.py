@@ -11,6 +11,9 @@ numpy arrays in the layout the attention calls take (int32; page_table
     s.push_token(7, next_token)       # once its prompt is complete
     b = s.decode_batch()
     s.finish(7)                       # its whole pages join the prefix cache
+
+A batch counts its new tokens as stored when it is built: run its store before
+finishing a request it extended.
 """
 from __future__ import annotations
 

@@ -167,3 +167,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pka, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         pka.lib()
+
+
+def test_scheduler_null_and_shape_checks(L):
+    from paged_kv_attention_25_amd import sched as S
+    S._lib()
+    h = ctypes.c_void_p()
+    assert L.pka_sched_create(1, 16, 1, 8, None) == pka.PKA_E_NULLPTR
+    assert L.pka_sched_create(1, 16, 2, 8, ctypes.byref(h)) == pka.PKA_E_SHAPE   # policy
+    assert L.pka_sched_create(1 << 16, 1 << 16, 1, 8, ctypes.byref(h)) == pka.PKA_E_SHAPE
+    assert L.pka_sched_create(1, 16, 1, 8, ctypes.byref(h)) == pka.PKA_OK
+    try:
+        assert L.pka_sched_add_request(None, 1, FAKE, 1) == pka.PKA_E_NULLPTR
+        assert L.pka_sched_add_request(h, 1, None, 1) == pka.PKA_E_NULLPTR
+        assert L.pka_sched_prefill_batch(h, None) == pka.PKA_E_NULLPTR
+        assert L.pka_sched_decode_batch(h, None) == pka.PKA_E_NULLPTR
+        b = S._Batch(4, 0, 4, 0, *([None] * 7), 0, 0, 0, 0)
+        assert L.pka_sched_prefill_batch(h, ctypes.byref(b)) == pka.PKA_E_SHAPE  # width 0
+        b = S._Batch(4, 4, 4, 0, *([None] * 7), 0, 0, 0, 0)
+        assert L.pka_sched_prefill_batch(h, ctypes.byref(b)) == pka.PKA_E_NULLPTR
+        assert L.pka_sched_push_tokens(h, None, None, -1) == pka.PKA_E_SHAPE
+        assert L.pka_sched_push_tokens(h, None, None, 0) == pka.PKA_OK
+        assert L.pka_sched_get_stats(h, None) == pka.PKA_E_NULLPTR
+    finally:
+        L.pka_sched_destroy(h)
+    L.pka_sched_destroy(None)
