@@ -66,7 +66,14 @@ def prefill_flops(part, step):
     return 4 * step.head_dim * step.num_q_heads * pairs
 
 
+def decode_flops(part, step):
+    """4*D flops per (query, key) pair per q head, for context (decode is HBM-bound)."""
+    return 4 * step.head_dim * step.num_q_heads * int(part.seq_lens.astype(np.int64).sum())
+
+
 def prefill_bytes(part, step):
+    """K+V rows of every referenced key plus q and out, for context (prefill is
+    MFMA-bound)."""
     d, hkv, hq = step.head_dim, step.num_kv_heads, step.num_q_heads
     seq = part.seq_lens.astype(np.int64)
     return int(seq.sum()) * hkv * d * 4 + 2 * part.num_tokens * hq * d * 2
@@ -390,12 +397,14 @@ def time_part(name, steps, warmup, flush, log):
             rec["decode_us"] = round(us, 2)
             rec["decode_GBs"] = round(gbs, 1)
             rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+            rec["decode_TFLOPs_context"] = round(decode_flops(p, st) / (us * 1e-6) / 1e12, 2)
         else:
             tf = prefill_flops(p, st) / (us * 1e-6) / 1e12
             rec["prefill_us"] = round(us, 2)
             rec["prefill_TFLOPs"] = round(tf, 1)
             rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
             rec["prefill_flops"] = prefill_flops(p, st)
+            rec["prefill_GBs_context"] = round(prefill_bytes(p, st) / (us * 1e-6) / 1e9, 1)
     if r.fused:
         rec["unfused_step_us"] = round(tot_u * 1e3, 2)   # store_kv, then decode
     if name == "tiny_decode":
@@ -614,6 +623,8 @@ def main():
                                "step = decode_store (split decode with the store of the 256 "
                                "new rows inside) + merge",
                    "batch": part.batch, "sum_context": int(part.seq_lens.sum()),
+                   "decode_TFLOPs_context": round(decode_flops(part, step) /
+                                                  (total_ms * 1e-3) / 1e12, 2),
                    "timing": "HIP events on the launch stream, caches flushed before each step; "
                              "median over the timed steps",
                    "wall_s_timed_region_incl_flush": round(wall, 4)},
