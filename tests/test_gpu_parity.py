@@ -229,6 +229,13 @@ def test_decode_store_b256_full():
     run_decode_store_case(W.decode_b256(device="cuda"), "decode_b256 all requests")
 
 
+@pytest.mark.parametrize("P", [16, 64])
+def test_decode_store_b256_page_sizes_sampled(P):
+    # the page-size sweep's launch: decode_b256 in pages of P slots, store inside
+    run_decode_store_case(W.decode_b256(device="cuda", page_size=P), f"decode_b256 P={P}",
+                          requests=list(range(5, 256, 16)))
+
+
 def test_decode_store_long_sampled():
     run_decode_store_case(W.long_decode(device="cuda"), "long_decode (6 requests)",
                           requests=[0, 7, 12, 19, 25, 31])
