@@ -7,6 +7,7 @@
  *   pka_store_kv            new K/V rows -> their slots in the K/V pools
  *   pka_paged_attn_prefill  causal extend (chunked) prefill on top of a cached prefix
  *   pka_paged_attn_decode   batched GQA decode, split over the key axis, then merged
+ *                           (small calls: one launch, merged on chip)
  *
  * and pka_paged_attn_decode_store, a decode step's store and decode in one launch.
  *
@@ -129,7 +130,10 @@ int pka_store_kv(const pka_geom* geom, const void* k_new, const void* v_new,
  *                 that run concurrently must not share a workspace.
  * Supported: D == 128, Hq/Hkv <= 16, batch <= 4096 and
  * batch * Hkv * ceil(max_seq_len / 64) < 2^31 (else PKA_E_UNSUPPORTED).
- * batch == 0 is a no-op.
+ * batch == 0 is a no-op. When ceil(max_seq_len / 64) <= 8 and
+ * batch * Hkv * ceil(max_seq_len / 64) <= 2048 the call is one launch that merges a
+ * pair's key blocks on chip (the workspace is then not used); otherwise the keys of
+ * the batch are split between persistent wavefronts and a second launch merges them.
  */
 int pka_paged_attn_decode(const pka_geom* geom, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* page_table,

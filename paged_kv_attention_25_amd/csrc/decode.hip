@@ -522,6 +522,86 @@ void decode_split_kernel(DecodeKernelArgs p) {
   }
 }
 
+// Small launches (a pair has at most kSmallWaves blocks and the whole batch fits in
+// one round of resident wavefronts): one workgroup per (request, kv head) pair, one
+// wavefront per 64-key block of it. Each wavefront runs its block like a split-kernel
+// segment, leaves the normalised partial output and log2-sum-exp of its q heads in LDS,
+// and the workgroup merges them (the same combination as the merge kernel), so the step
+// needs neither the batch-wide block scan nor a second launch.
+constexpr int kSmallWaves = 8;  // 256 VGPRs per wavefront: two per SIMD
+constexpr int kSmallMaxTotalWaves = kMaxDecodeWaves;
+
+template <bool kStore>
+__global__ __launch_bounds__(kSmallWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_small_kernel(DecodeKernelArgs p) {
+  __shared__ float s_o[kSmallWaves * kMaxGroup][kHeadDim];
+  __shared__ float s_lse[kSmallWaves * kMaxGroup];
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+  const int32_t b = uniform((int32_t)blockIdx.x / p.num_kv_heads);
+  const int32_t g = uniform((int32_t)blockIdx.x - b * p.num_kv_heads);
+  const int32_t L = uniform(min(p.seq_lens[b], p.max_seq_len));
+  if (L <= 0) return;  // no keys: the output row is not written (as in the split path)
+  Desc d;
+  d.b = b;
+  d.g = g;
+  d.L = L;
+  d.k0 = wave * kBlock;
+  d.end = L;
+  d.valid = d.k0 < L;
+  d.last = 1;
+  d.slot = -1;
+  d.tail = d.valid && L <= d.k0 + kBlock;
+  SoftmaxState st;
+  reset_state(st);
+  if (d.valid) {
+    const RawSlot raw = lookup_raw<kStore>(d, lane, p);
+    const int32_t slot = resolve(raw, p);
+    if (kStore) store_new_row(d, raw, lane, p);
+    Block blk;
+    load_block<true, true>(blk, d, slot, n, grp, p);
+    u32x4 pbs[2];
+    scores_softmax(blk, d, grp, p.scale_log2, st, pbs);
+    pv_block(blk, pbs, st);
+    float ltot = st.lsum + __shfl_xor(st.lsum, 16);
+    ltot += __shfl_xor(ltot, 32);
+    if (n < p.group) {
+      // lane (n, grp) holds d = 32*grp + 8v + t of q head n in o[t][v]
+      const int row = wave * p.group + n;
+      const float inv = 1.f / ltot;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s_o[row][32 * grp + 8 * v + t] = st.o[t][v] * inv;
+      if (grp == 0) s_lse[row] = st.m + __builtin_log2f(ltot);
+    }
+  }
+  __syncthreads();
+  // Merge: thread i combines output element i of the pair's G x D (two per thread).
+  const int nblk = blocks_of(L);  // wavefronts that wrote a partial (>= 1)
+  const int pairs = p.group * (kHeadDim / 2);
+  for (int i = tid; i < pairs; i += (int)blockDim.x) {
+    const int hn = i / (kHeadDim / 2);
+    const int dd = 2 * (i - hn * (kHeadDim / 2));
+    float mx = kNegInf;
+    for (int w = 0; w < nblk; ++w) mx = fmaxf(mx, s_lse[w * p.group + hn]);
+    float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+    for (int w = 0; w < nblk; ++w) {
+      const int row = w * p.group + hn;
+      const float wt = fast_exp2(s_lse[row] - mx);
+      wsum += wt;
+      acc0 += wt * s_o[row][dd];
+      acc1 += wt * s_o[row][dd + 1];
+    }
+    const float inv = 1.f / wsum;
+    uint16_t* dst = p.out + ((int64_t)b * p.num_q_heads + (int64_t)g * p.group + hn) * kHeadDim + dd;
+    *(uint32_t*)dst = pack_bf16x2(acc0 * inv, acc1 * inv);
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -666,7 +746,9 @@ DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32
   plan.groups = (int32_t)groups;
   plan.waves = (int32_t)(groups * num_kv_heads);
   plan.splits = per_pair > 1;
-  (void)group;
+  plan.small_waves = (int32_t)per_pair;
+  plan.small = per_pair >= 1 && per_pair <= kSmallWaves && group <= kMaxGroup &&
+               (int64_t)batch * num_kv_heads * per_pair <= kSmallMaxTotalWaves;
   return plan;
 }
 
@@ -706,6 +788,15 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   k.k_dst = (uint16_t*)a.k_dst;
   k.v_dst = (uint16_t*)a.v_dst;
   k.num_slots = a.num_pages * (int64_t)a.page_size;
+  if (plan.small) {
+    const dim3 grid((unsigned)((int64_t)a.batch * a.num_kv_heads));
+    const dim3 block((unsigned)(plan.small_waves * 64));
+    if (k.k_new)
+      hipLaunchKernelGGL(decode_small_kernel<true>, grid, block, 0, stream, k);
+    else
+      hipLaunchKernelGGL(decode_small_kernel<false>, grid, block, 0, stream, k);
+    return hipGetLastError();
+  }
   const int grid = (plan.waves + kWaves - 1) / kWaves;
   if (k.k_new)
     hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0,

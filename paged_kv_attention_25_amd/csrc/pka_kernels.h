@@ -29,6 +29,10 @@ struct DecodePlan {
   int32_t groups;
   int32_t waves;
   bool splits;
+  // One launch: a workgroup per (request, kv head), a wavefront per 64-key block of it
+  // (small_waves of them), the blocks merged in LDS; the workspace is not used.
+  bool small;
+  int32_t small_waves;
 };
 DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_seq_len);
 // Whether the decode kernel supports this shape: batch, group size (q heads per kv

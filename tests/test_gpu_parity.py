@@ -195,6 +195,31 @@ def test_decode_split_count_invariance():
     assert_close(a, oracle.bf16_bits_to_f64(b), "alone vs in the batch")
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (16, 8), (40, 8)])
+def test_decode_one_launch_and_split_paths_agree(hq, hkv):
+    # Lengths up to 512 keys. With a max_seq_len hint of 512 the call runs in one launch
+    # (a workgroup per (request, kv head), one wavefront per 64-key block, merged in LDS;
+    # 8 wavefronts at the limit); with a hint of 1024 it takes the split kernel and its
+    # merge launch. Both must match the oracle.
+    lens = [1, 63, 64, 65, 200, 511, 512]
+    pages = sum(-(-L // 16) for L in lens) + 8
+    step = W.build_step("paths", hq, hkv, 16, pages, [W.decode_spec(lens)], seed=51,
+                        device="cuda")
+    part = step.parts[0]
+    # room in the table for the 1024-key hint (columns past a request's pages are
+    # never read)
+    part.page_table = np.pad(part.page_table, ((0, 0), (0, 1024 // 16)))
+    host = HostInputs(step)
+    check_store(step, host, "paths")
+    announce(f"decode one-launch vs split paths hq={hq} hkv={hkv}")
+    one = host_u16(gpu_part(step, part, max_seq_len=512))
+    split = host_u16(gpu_part(step, part, max_seq_len=1024))
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(step, host, 0)
+    assert_close(one, ref, f"one launch hq={hq} hkv={hkv}")
+    assert_close(split, ref, f"split hq={hq} hkv={hkv}")
+
+
 # --- store and decode in one launch ------------------------------------------------------
 
 def check_pools(step, host, what):
@@ -234,6 +259,16 @@ def test_decode_store_b256_page_sizes_sampled(P):
     # the page-size sweep's launch: decode_b256 in pages of P slots, store inside
     run_decode_store_case(W.decode_b256(device="cuda", page_size=P), f"decode_b256 P={P}",
                           requests=list(range(5, 256, 16)))
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (40, 8)])
+def test_decode_store_one_launch_path(hq, hkv):
+    # the store inside the one-launch path, 8 wavefronts per pair at the limit
+    lens = [1, 64, 65, 300, 512]
+    pages = sum(-(-L // 16) for L in lens) + 8
+    step = W.build_step("paths", hq, hkv, 16, pages, [W.decode_spec(lens)], seed=53,
+                        device="cuda")
+    run_decode_store_case(step, f"one launch hq={hq} hkv={hkv}", max_seq_len=512)
 
 
 def test_decode_store_long_sampled():
