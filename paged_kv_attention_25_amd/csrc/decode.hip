@@ -62,7 +62,10 @@ constexpr int kBlock = 64;        // keys per wavefront block
 constexpr int kWaves = 4;         // wavefronts per workgroup (sharing the LDS tables)
 constexpr int kMaxBatchLds = 4096;
 constexpr int kMaxGroup = 16;
-constexpr int kMaxDecodeWaves = 2048;  // resident wavefronts: 256 CUs x 4 SIMDs x 2
+// Wavefronts of the split kernel: one per SIMD (256 CUs x 4), one 4-wavefront workgroup
+// per CU. Measured on decode_b256 / long_decode / tp4_mixed: 1024 beats 2048 (two per
+// SIMD) by 1-2%; 1536 (half the CUs with two workgroups) and 512 are 11% and 35% slower.
+constexpr int kMaxDecodeWaves = 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct DecodeKernelArgs {
@@ -529,7 +532,7 @@ void decode_split_kernel(DecodeKernelArgs p) {
 // and the workgroup merges them (the same combination as the merge kernel), so the step
 // needs neither the batch-wide block scan nor a second launch.
 constexpr int kSmallWaves = 8;  // 256 VGPRs per wavefront: two per SIMD
-constexpr int kSmallMaxTotalWaves = kMaxDecodeWaves;
+constexpr int kSmallMaxTotalWaves = 2048;
 
 template <bool kStore>
 __global__ __launch_bounds__(kSmallWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))

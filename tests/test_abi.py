@@ -77,15 +77,15 @@ def test_workspace_sizes(L):
     assert L.pka_decode_workspace_bytes(ctypes.byref(g), 1, 64) == 0
     # otherwise 2 partial slots per wavefront (G rows of D floats + lse each) and the
     # block prefix sums over the batch; wavefronts = Hkv x groups, groups =
-    # min(floor(2048 / Hkv), blocks one kv head of the batch can have)
+    # min(floor(1024 / Hkv), blocks one kv head of the batch can have)
     G = 2
     assert L.pka_decode_workspace_bytes(ctypes.byref(g), 32, 32768) == \
-        2 * 2048 * G * 129 * 4 + 33 * 4
+        2 * 1024 * G * 129 * 4 + 33 * 4
     assert L.pka_decode_workspace_bytes(ctypes.byref(g), 4, 100) == \
         2 * (4 * 8 * 2) * G * 129 * 4 + 5 * 4
-    g3 = geom(num_q_heads=6, num_kv_heads=3)                        # 682 groups of 3
+    g3 = geom(num_q_heads=6, num_kv_heads=3)                        # 341 groups of 3
     assert L.pka_decode_workspace_bytes(ctypes.byref(g3), 32, 32768) == \
-        2 * 2046 * G * 129 * 4 + 33 * 4
+        2 * 1023 * G * 129 * 4 + 33 * 4
     assert L.pka_decode_workspace_bytes(None, 4, 100) == 0
     # prefill: one int32 per (request, 256-row q tile) item when batch > 1, else 0
     assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 1, 10, 6) == 0
