@@ -174,6 +174,48 @@ def test_planted_missing_cap_fails_the_closed_form():
     assert [(r, p) for r, p, _ in rows] != [(1, closed)]
 
 
+def test_oracle_chunk_budget_closed_form():
+    # One 20000-token prompt under an 8192-token budget is prefilled as 8192 + 8192 + 3616
+    # (deployment guide, section 6.1: chunks of at most max-prefill-length tokens); a
+    # second request joins the batch that has budget left.
+    ref = PrefixCacheRef(16, 4096, "radix", 8192)
+    ref.add_request(1, [t % 1000 for t in range(20000)])
+    ref.add_request(2, [5000 + t for t in range(100)])
+    got = [ref.prefill_batch(8, 1 << 30) for _ in range(3)]
+    assert got == [[(1, 0, 8192)], [(1, 8192, 8192)], [(1, 16384, 3616), (2, 0, 100)]]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_oracle_naive_policy_closed_form(seed):
+    # The naive manager shares nothing: nothing is ever cached or evicted, every
+    # admission matches 0 tokens, and free + private pages always make up the pool.
+    rng = random.Random(seed)
+    ref = PrefixCacheRef(4, 50, "naive", 40)
+    live, nid = [], 0
+    for _ in range(400):
+        op = rng.random()
+        if op < 0.3 and len(live) < 8:
+            ref.add_request(nid, [rng.randrange(3) for _ in range(rng.randrange(1, 40))])
+            live.append(nid)
+            nid += 1
+        elif op < 0.6:
+            ref.prefill_batch(8, 1 << 30)
+        elif op < 0.8:
+            for rid in live:
+                r = ref.reqs[rid]
+                if r["state"] == "running" and not r["pending"]:
+                    ref.push_token(rid, rng.randrange(3))
+            ref.decode_batch(8, 1 << 30)
+        elif live:
+            ref.finish(live.pop(rng.randrange(len(live))))
+        st = ref.stats()
+        assert st["cached_pages"] == 0 and st["evicted_pages"] == 0 and st["locked_pages"] == 0
+        assert st["free_pages"] + st["private_pages"] == 50
+        for rid in live:
+            r = ref.reqs[rid]
+            assert r["matched"] == [] and r["pages"] == -(-r["cached"] // 4)
+
+
 # --- the library against the oracle ----------------------------------------------------
 
 
