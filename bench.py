@@ -198,6 +198,41 @@ def time_step(runner, steps, warmup, flush, cold=True):
     return seg, total, wall
 
 
+def two_stream_step_us(runner, steps, warmup, flush):
+    """A mixed step (a decode part and a prefill part) with the decode on a second
+    stream: store_kv on the launch stream, then the decode on the second stream (after
+    the store) beside the prefill on the launch stream; the step ends when both have.
+    Both streams run at the default priority. Median step time, µs, over `steps`
+    cold-cache steps."""
+    import torch
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    kinds = [p.kind for p in runner.step.parts]
+    di, pi = kinds.index("decode"), kinds.index("prefill")
+
+    def calls():
+        runner.store()
+        stored = torch.cuda.Event()
+        stored.record(s1)
+        with torch.cuda.stream(s2):
+            s2.wait_event(stored)
+            runner.attend(di)
+        runner.attend(pi)
+        s1.wait_stream(s2)
+
+    for _ in range(warmup):
+        calls()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        flush()
+        ev[k][0].record()
+        calls()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
 def graph_step_us(runner, steps, flush):
     """The whole step (store + every attention part) captured once as a HIP graph and
     replayed: median µs per replay, caches flushed before each (launch overhead of the
@@ -409,6 +444,10 @@ def time_part(name, steps, warmup, flush, log):
         rec["unfused_step_us"] = round(tot_u * 1e3, 2)   # store_kv, then decode
     if name == "tiny_decode":
         rec["graph_step_us"] = round(graph_step_us(r, steps, flush), 2)
+    kinds = {p.kind for p in st.parts}
+    if kinds == {"decode", "prefill"}:
+        # the same step with the decode beside the prefill on a second stream
+        rec["two_stream_step_us"] = round(two_stream_step_us(r, steps, 10, flush), 2)
     log(f"{name}: {rec}")
     del r, st
     torch.cuda.empty_cache()

@@ -533,6 +533,32 @@ def test_prefill_block_tile_counts(tiles, batch):
     run_prefill_case(step, f"tiles={tiles} batch={batch}")
 
 
+def test_mixed_step_on_two_streams_matches_one_stream():
+    # The mixed step with its decode on a second stream beside the prefill (after the
+    # store) gives outputs bit-identical to the one-stream order store, decode, prefill.
+    step = W.build_step("mixed", 16, 2, 1, 1 << 17,
+                        [W.decode_spec(list(range(300, 300 + 64 * 37, 37))),
+                         ("prefill", [512], [2048])], seed=61, device="cuda", fill="zero")
+    dec, pre = step.parts
+    announce("mixed step: two streams vs one")
+    gpu_store(step)
+    d1 = gpu_part(step, dec)
+    p1 = gpu_part(step, pre)
+    torch.cuda.synchronize()
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    gpu_store(step)  # the same rows again: the pools do not change
+    stored = torch.cuda.Event()
+    stored.record(s1)
+    with torch.cuda.stream(s2):
+        s2.wait_event(stored)
+        d2 = gpu_part(step, dec)
+    p2 = gpu_part(step, pre)
+    s1.wait_stream(s2)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(p1, p2)
+
+
 def test_step_graph_replay_matches_eager():
     """store + decode + prefill captured once in a HIP graph and replayed three times,
     with eager work and synchronisation between replays: every replay reproduces the
