@@ -512,12 +512,9 @@ def host_sched_bench(log, decode_steps=20):
     first, second = prompts(), prompts()
     nxt = rng.integers(0, 32000, (decode_steps, B)).astype(np.int32)
     s = S.Scheduler(1, 1 << 20, "radix", 8192, max_batch=B, table_width=W, max_tokens=8192)
-    L, h, bufs = s._L, s._h, s._bufs
+    L, h, c, bufs = s.raw()
     for a in bufs.values():   # fault the output buffers in before timing
         a.fill(1)
-    c = S._Batch(B, W, 8192, 0, *(bufs[k].ctypes.data for k in (
-        "req_ids", "page_table", "seq_lens", "prefix_lens", "extend_lens", "cu_extend",
-        "out_loc")), 0, 0, 0, 0)
     ids = np.arange(B, dtype=np.int64)
     tc = time.perf_counter
 
@@ -526,7 +523,7 @@ def host_sched_bench(log, decode_steps=20):
         for i, p in enumerate(reqs):
             L.pka_sched_add_request(h, offset + i, p.ctypes.data, int(p.size))
         t1 = tc()
-        nb, reused = 0, 0
+        nb = 0
         while True:
             assert L.pka_sched_prefill_batch(h, ctypes.byref(c)) == 0
             if c.batch == 0:

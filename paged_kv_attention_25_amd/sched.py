@@ -178,13 +178,24 @@ class Scheduler:
         _check(self._L.pka_sched_add_request(self._h, int(req_id), t.ctypes.data, int(t.size)),
                "pka_sched_add_request")
 
+    def _descriptor(self) -> _Batch:
+        b = self._bufs
+        return _Batch(self.max_batch, self.table_width, self.max_tokens, 0,
+                      b["req_ids"].ctypes.data, b["page_table"].ctypes.data,
+                      b["seq_lens"].ctypes.data, b["prefix_lens"].ctypes.data,
+                      b["extend_lens"].ctypes.data, b["cu_extend"].ctypes.data,
+                      b["out_loc"].ctypes.data, 0, 0, 0, 0)
+
+    def raw(self):
+        """(library, handle, batch descriptor, buffers) for calling the C entry points
+        directly, e.g. to time them without the Python-side copies: the descriptor points
+        at this object's preallocated host buffers (a dict of numpy arrays), which the
+        batch calls fill in place."""
+        return self._L, self._h, self._descriptor(), self._bufs
+
     def _batch(self, fn, what) -> Batch:
         b = self._bufs
-        c = _Batch(self.max_batch, self.table_width, self.max_tokens, 0,
-                   b["req_ids"].ctypes.data, b["page_table"].ctypes.data,
-                   b["seq_lens"].ctypes.data, b["prefix_lens"].ctypes.data,
-                   b["extend_lens"].ctypes.data, b["cu_extend"].ctypes.data,
-                   b["out_loc"].ctypes.data, 0, 0, 0, 0)
+        c = self._descriptor()
         _check(fn(self._h, ctypes.byref(c)), what)
         n, t = c.batch, c.num_tokens
         return Batch(b["req_ids"][:n].copy(), b["page_table"][:n].copy(), b["seq_lens"][:n].copy(),
