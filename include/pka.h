@@ -157,13 +157,15 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
  *                 [0, num_pages*P) is skipped, as in pka_store_kv.
  *   k_pool, v_pool  the pools (device), read and updated in place
  *   other arguments, workspace size and support as in pka_paged_attn_decode.
- * Where the page table maps request b's key L_b - 1 to slot out_loc[b] (the usual
- * decode step), that key is read from k_new / v_new; every other key is read from the
- * pools. The slots in out_loc must be pairwise distinct and must not be read as another
- * request's keys in the same call (new tokens' slots are private to their request);
- * then the result equals the two calls' bit for bit in the pools and within rounding
- * order in out. The store of request b is made by the wavefront that reads its last
- * key block, so it needs L_b >= 1 (as decode does).
+ * Every key, including key L_b - 1, is read from the pools: the wavefront that reads
+ * request b's last key block first writes the new rows to slot out_loc[b] and then
+ * issues that block's loads, which see its own stores, so where the page table maps
+ * key L_b - 1 to slot out_loc[b] (the usual decode step) the new rows are what it
+ * attends to. The slots in out_loc must be pairwise distinct and must not be read as
+ * another request's keys in the same call (new tokens' slots are private to their
+ * request); then the result equals the two calls' bit for bit in the pools and within
+ * rounding order in out. The store of request b is made by the wavefront that reads its
+ * last key block, so it needs L_b >= 1 (as decode does).
  */
 int pka_paged_attn_decode_store(const pka_geom* geom, const void* q, const void* k_new,
                                 const void* v_new, const int32_t* out_loc, void* k_pool,

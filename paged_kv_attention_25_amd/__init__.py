@@ -12,9 +12,19 @@ Functions (same names as the C entry points, without the ``pka_`` prefix):
   paged_attn_prefill(q, k_pool, v_pool, page_table, seq_lens, prefix_lens, extend_lens,
                      cu_extend, max_extend, max_seq_len, page_size, scale, out=None,
                      workspace=None)
+  paged_attn_decode_store(q, k_new, v_new, out_loc, ...)
   decode_workspace_bytes(...), prefill_workspace_bytes(...)
 Tensor conventions: bf16 tensors may be torch.bfloat16 or int16/uint16 bit
-patterns; index tensors are int32; all tensors contiguous on the same GPU.
+patterns; index tensors are int32; all tensors contiguous on the same GPU. Each call
+checks these conventions and the shape relations between its tensors on the host
+before anything reaches the library, and raises ValueError on a mismatch (a CPU
+tensor or a short metadata array would otherwise become a bad device pointer).
+
+Debug mode (``PKA_DEBUG=1`` in the environment or ``set_debug(True)``): each call
+also copies its device metadata to the host and checks it (``checks.py``: page ids
+inside the pool, lengths within the host-known bounds, distinct and private
+new-token slots), raising ``checks.MetadataError`` before any launch. It
+synchronises with the device; leave it off when timing.
 """
 from __future__ import annotations
 
@@ -121,6 +131,19 @@ def _check(status: int, what: str):
         raise PkaError(status, what)
 
 
+_debug = os.environ.get("PKA_DEBUG", "0") not in ("", "0")
+
+
+def set_debug(on: bool) -> None:
+    """Turn the host-side metadata checks of every call on or off."""
+    global _debug
+    _debug = bool(on)
+
+
+def debug_enabled() -> bool:
+    return _debug
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -135,19 +158,86 @@ def make_geom(num_q_heads, num_kv_heads, head_dim, page_size, num_pages) -> Geom
                 int(num_pages))
 
 
-def _pool_geom(q_heads, k_pool, page_size) -> Geom:
-    slots, hkv, d = k_pool.shape
-    if slots % page_size:
-        raise ValueError("pool slots must be a whole number of pages")
-    return make_geom(q_heads, hkv, d, page_size, slots // page_size)
+# --- host-side tensor checks ------------------------------------------------------------
+
+def _tensor(t, name, kind, shape):
+    """`t` must be a contiguous torch tensor of `kind` ("bf16": bfloat16 or 16-bit
+    integer bit patterns; "i32"; "bytes": any dtype) whose shape matches `shape`
+    (None entries match any size)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if kind == "bf16" and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"{name} must hold bf16 values (torch.bfloat16 or 16-bit bit "
+                         f"patterns), got {t.dtype}")
+    if kind == "i32" and t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(s) != int(w)
+                                        for s, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_gpu(named):
+    """Every tensor in `named` ({name: tensor or None}) lives on one and the same GPU."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other tensors on {dev}")
+    return dev
+
+
+def _pools(k_pool, v_pool, page_size):
+    """Checks the two pools ([slots, Hkv, D], equal shapes, whole pages); returns
+    (Hkv, D, num_pages)."""
+    _tensor(k_pool, "k_pool", "bf16", (None, None, None))
+    _tensor(v_pool, "v_pool", "bf16", tuple(k_pool.shape))
+    if int(page_size) < 1:
+        raise ValueError(f"page_size must be >= 1, got {page_size}")
+    slots, hkv, d = (int(s) for s in k_pool.shape)
+    if slots % int(page_size):
+        raise ValueError(f"pool of {slots} slots is not a whole number of {page_size}-slot "
+                         "pages")
+    return hkv, d, slots // int(page_size)
+
+
+def _workspace(ws):
+    if ws is not None:
+        _tensor(ws, "workspace", "bytes", None)
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _out(out, like, name="out"):
+    if out is not None:
+        _tensor(out, name, "bf16", tuple(like.shape))
+        if out.data_ptr() == like.data_ptr():
+            raise ValueError(f"{name} must not alias q")
 
 
 def store_kv(k_new, v_new, out_loc, k_pool, v_pool, page_size=1):
     """pka_store_kv: k_pool[out_loc[t]] = k_new[t], v_pool[out_loc[t]] = v_new[t]."""
-    g = _pool_geom(k_pool.shape[1], k_pool, page_size)
-    _check(lib().pka_store_kv(ctypes.byref(g), _ptr(k_new), _ptr(v_new), _ptr(out_loc),
-                              int(out_loc.shape[0]), _ptr(k_pool), _ptr(v_pool),
-                              _stream(k_pool.device)), "pka_store_kv")
+    hkv, d, num_pages = _pools(k_pool, v_pool, page_size)
+    _tensor(out_loc, "out_loc", "i32", (None,))
+    rows = int(out_loc.shape[0])
+    _tensor(k_new, "k_new", "bf16", (rows, hkv, d))
+    _tensor(v_new, "v_new", "bf16", (rows, hkv, d))
+    if _debug:
+        from . import checks
+        checks.check_out_loc(out_loc, num_pages * int(page_size))
+    _same_gpu(dict(k_new=k_new, v_new=v_new, out_loc=out_loc, k_pool=k_pool, v_pool=v_pool))
+    g = make_geom(hkv, hkv, d, page_size, num_pages)
+    _check(lib().pka_store_kv(ctypes.byref(g), _ptr(k_new), _ptr(v_new), _ptr(out_loc), rows,
+                              _ptr(k_pool), _ptr(v_pool), _stream(k_pool.device)),
+           "pka_store_kv")
 
 
 def decode_workspace_bytes(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, batch,
@@ -168,19 +258,41 @@ def _alloc_like(q, nbytes):
     return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=q.device)
 
 
+def _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out, workspace,
+                   extra=None):
+    """Checks shared by the decode entry points; returns (geometry, batch, the tensors
+    by name for the device check)."""
+    hkv, d, num_pages = _pools(k_pool, v_pool, page_size)
+    _tensor(q, "q", "bf16", (None, None, d))
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    if hq % hkv:
+        raise ValueError(f"q has {hq} heads, not a multiple of the pools' {hkv} kv heads")
+    _tensor(page_table, "page_table", "i32", (batch, None))
+    _tensor(seq_lens, "seq_lens", "i32", (batch,))
+    _out(out, q)
+    _workspace(workspace)
+    named = dict(q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, seq_lens=seq_lens,
+                 out=out, workspace=workspace, **(extra or {}))
+    return make_geom(hq, hkv, d, page_size, num_pages), batch, named
+
+
 def paged_attn_decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, page_size, scale,
                       out=None, workspace=None):
     """pka_paged_attn_decode. q [B, Hq, D]; returns out [B, Hq, D] (same dtype as q).
     Without a workspace, one of pka_decode_workspace_bytes is allocated for the call."""
     import torch
-    g = _pool_geom(q.shape[1], k_pool, page_size)
-    batch = int(q.shape[0])
+    g, batch, named = _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out,
+                                     workspace)
+    if _debug:
+        from . import checks
+        checks.check_decode(seq_lens, int(max_seq_len), page_table, int(page_size), g.num_pages)
+    _same_gpu(named)
     if out is None:
         out = torch.empty_like(q)
     need = int(lib().pka_decode_workspace_bytes(ctypes.byref(g), batch, int(max_seq_len)))
     if workspace is None and need > 0:
         workspace = _alloc_like(q, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace(workspace)
     _check(lib().pka_paged_attn_decode(ctypes.byref(g), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                        _ptr(page_table), int(page_table.shape[1]),
                                        _ptr(seq_lens), batch, int(max_seq_len), float(scale),
@@ -189,20 +301,35 @@ def paged_attn_decode(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, page
     return out
 
 
+def _new_rows(k_new, v_new, out_loc, batch, hkv, d):
+    _tensor(k_new, "k_new", "bf16", (batch, hkv, d))
+    _tensor(v_new, "v_new", "bf16", (batch, hkv, d))
+    _tensor(out_loc, "out_loc", "i32", (batch,))
+    return dict(k_new=k_new, v_new=v_new, out_loc=out_loc)
+
+
 def paged_attn_decode_store(q, k_new, v_new, out_loc, k_pool, v_pool, page_table, seq_lens,
                             max_seq_len, page_size, scale, out=None, workspace=None):
     """pka_paged_attn_decode_store: stores k_new[b], v_new[b] [B, Hkv, D] into slot
     out_loc[b] of the pools and decodes, in one launch (the same result as store_kv then
     paged_attn_decode). Returns out [B, Hq, D]."""
     import torch
-    g = _pool_geom(q.shape[1], k_pool, page_size)
-    batch = int(q.shape[0])
+    hkv, d, _ = _pools(k_pool, v_pool, page_size)
+    _tensor(q, "q", "bf16", (None, None, d))
+    extra = _new_rows(k_new, v_new, out_loc, int(q.shape[0]), hkv, d)
+    g, batch, named = _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out,
+                                     workspace, extra)
+    if _debug:
+        from . import checks
+        checks.check_decode_store(out_loc, seq_lens, int(max_seq_len), page_table,
+                                  int(page_size), g.num_pages)
+    _same_gpu(named)
     if out is None:
         out = torch.empty_like(q)
     need = int(lib().pka_decode_workspace_bytes(ctypes.byref(g), batch, int(max_seq_len)))
     if workspace is None and need > 0:
         workspace = _alloc_like(q, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace(workspace)
     _check(lib().pka_paged_attn_decode_store(ctypes.byref(g), _ptr(q), _ptr(k_new),
                                              _ptr(v_new), _ptr(out_loc), _ptr(k_pool),
                                              _ptr(v_pool), _ptr(page_table),
@@ -218,16 +345,35 @@ def paged_attn_prefill(q, k_pool, v_pool, page_table, seq_lens, prefix_lens, ext
                        workspace=None):
     """pka_paged_attn_prefill. q [T, Hq, D]; returns out [T, Hq, D] (same dtype as q)."""
     import torch
-    g = _pool_geom(q.shape[1], k_pool, page_size)
+    hkv, d, num_pages = _pools(k_pool, v_pool, page_size)
+    _tensor(q, "q", "bf16", (None, None, d))
+    tokens, hq = int(q.shape[0]), int(q.shape[1])
+    if hq % hkv:
+        raise ValueError(f"q has {hq} heads, not a multiple of the pools' {hkv} kv heads")
+    _tensor(seq_lens, "seq_lens", "i32", (None,))
     batch = int(seq_lens.shape[0])
-    tokens = int(q.shape[0])
+    _tensor(prefix_lens, "prefix_lens", "i32", (batch,))
+    _tensor(extend_lens, "extend_lens", "i32", (batch,))
+    _tensor(cu_extend, "cu_extend", "i32", (batch + 1,))
+    _tensor(page_table, "page_table", "i32", (batch, None))
+    _out(out, q)
+    _workspace(workspace)
+    if _debug:
+        from . import checks
+        checks.check_prefill(seq_lens, prefix_lens, extend_lens, cu_extend, tokens,
+                             int(max_extend), int(max_seq_len), page_table, int(page_size),
+                             num_pages)
+    _same_gpu(dict(q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, seq_lens=seq_lens,
+                   prefix_lens=prefix_lens, extend_lens=extend_lens, cu_extend=cu_extend,
+                   out=out, workspace=workspace))
+    g = make_geom(hq, hkv, d, page_size, num_pages)
     if out is None:
         out = torch.empty_like(q)
     need = int(lib().pka_prefill_workspace_bytes(ctypes.byref(g), batch, tokens,
                                                  int(max_extend)))
     if workspace is None and need > 0:
         workspace = _alloc_like(q, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace(workspace)
     _check(lib().pka_paged_attn_prefill(ctypes.byref(g), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                         _ptr(page_table), int(page_table.shape[1]),
                                         _ptr(seq_lens), _ptr(prefix_lens), _ptr(extend_lens),

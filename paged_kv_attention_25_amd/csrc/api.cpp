@@ -187,7 +187,8 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
   const int64_t pages_needed = ((int64_t)max_seq_len + geom->page_size - 1) / geom->page_size;
   if (page_table_stride < pages_needed) return PKA_E_SHAPE;
   const int64_t group = geom->num_q_heads / geom->num_kv_heads;
-  const int64_t tiles = ((int64_t)max_extend * group + 127) / 128;
+  const int64_t tiles =
+      ((int64_t)max_extend * group + pka::kPrefillRowsPerBlock - 1) / pka::kPrefillRowsPerBlock;
   if (tiles * batch * geom->num_kv_heads > 0x7fffffffLL) return PKA_E_UNSUPPORTED;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !prefix_lens || !extend_lens ||
       !cu_extend || !out)

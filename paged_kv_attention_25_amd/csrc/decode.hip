@@ -68,10 +68,12 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxDecodeWaves = 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// The pool pointers carry no __restrict__: with the store (kStore) the same pools are
+// written through k_dst / v_dst in the same launch.
 struct DecodeKernelArgs {
   const uint16_t* __restrict__ q;
-  const uint16_t* __restrict__ k_pool;
-  const uint16_t* __restrict__ v_pool;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
   const int32_t* __restrict__ page_table;
   const int32_t* __restrict__ seq_lens;
   uint16_t* __restrict__ out;

@@ -67,6 +67,10 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Query rows (token, q head of the kv head's group) one prefill workgroup owns; a
+// request gets ceil(max_extend * G / kPrefillRowsPerBlock) work items per kv head.
+constexpr int kPrefillRowsPerBlock = 256;
+
 struct PrefillArgs {
   const void* q;
   const void* k_pool;

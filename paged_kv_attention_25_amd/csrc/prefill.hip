@@ -53,6 +53,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 256
+static_assert(kRowsPerBlock == kPrefillRowsPerBlock, "work items are sized by the launcher");
 constexpr int kKeysPerTile = 64;
 constexpr int kLoaders = kWaves / 2;                   // wavefronts that load tiles
 constexpr int kKeysPerWave = kKeysPerTile / kLoaders;  // keys of a tile each loader loads
