@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from paged_kv_attention_25_amd import workloads as W
-from tests.gpu_common import (HostInputs, announce, assert_close, gpu_decode_store, gpu_part,
-                              gpu_store, host_u16, oracle_decode, oracle_prefill)
+from tests.gpu_common import (HostInputs, announce, assert_close, dev_i32, gpu_decode_store,
+                              gpu_part, gpu_store, host_u16, oracle_decode, oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,10 +92,9 @@ def test_decode_b256_page_sizes_sampled(P):
     run_decode_case(step, f"decode_b256 P={P} (16 requests)", requests=list(range(3, 256, 16)))
 
 
-def test_decode_long_sampled():
+def test_decode_long_full():
     step = W.long_decode(device="cuda")
-    run_decode_case(step, "long_decode 32x32768 P=64 (8 requests)", requests=[0, 5, 9, 13, 18,
-                                                                              22, 27, 31])
+    run_decode_case(step, "long_decode 32x32768 P=64 (all 32 requests)")
 
 
 def test_decode_tp4_part():
@@ -271,9 +270,8 @@ def test_decode_store_one_launch_path(hq, hkv):
     run_decode_store_case(step, f"one launch hq={hq} hkv={hkv}", max_seq_len=512)
 
 
-def test_decode_store_long_sampled():
-    run_decode_store_case(W.long_decode(device="cuda"), "long_decode (6 requests)",
-                          requests=[0, 7, 12, 19, 25, 31])
+def test_decode_store_long_full():
+    run_decode_store_case(W.long_decode(device="cuda"), "long_decode (all 32 requests)")
 
 
 @pytest.mark.parametrize("hq,hkv,page_size,lens", [
@@ -430,6 +428,20 @@ def test_prefill_chunked_sampled():
                      windows=windows)
 
 
+def test_prefill_chunked_full():
+    """Every output row of the chunked_prefill workload (32 requests, 8192 new tokens,
+    40q/8kv, P=16) against the oracle."""
+    run_prefill_case(W.chunked_prefill(device="cuda"),
+                     "chunked_prefill 32 req, 8192 tokens, P=16 (every row)")
+
+
+def test_prefill_tp4_chunk_full():
+    """Every output row of the tensor-parallel step's 8192-token chunk on a 1024-token
+    prefix (16q/2kv, P=1) against the oracle."""
+    run_prefill_case(W.tp4_mixed(device="cuda"),
+                     "tp4_mixed 8192-token chunk on 1024 prefix (every row)", part_idx=1)
+
+
 @pytest.mark.parametrize("P", [1, 32, 64])
 def test_prefill_chunked_page_sizes_sampled(P):
     # the chunked_prefill requests with the pool cut into other page sizes (the
@@ -534,20 +546,28 @@ def test_prefill_block_tile_counts(tiles, batch):
 
 
 def test_mixed_step_on_two_streams_matches_one_stream():
-    # The mixed step with its decode on a second stream beside the prefill (after the
-    # store) gives outputs bit-identical to the one-stream order store, decode, prefill.
+    """The mixed step with its decode on a second stream beside the prefill (the decode
+    waits for the store through an event) gives outputs bit-identical to the one-stream
+    order store, decode, prefill, and both match the oracle. The pools are put back to
+    their state before the first store (new tokens' slots NaN) before the two-stream
+    run, so a decode that ran before the store would read NaN."""
     step = W.build_step("mixed", 16, 2, 1, 1 << 17,
                         [W.decode_spec(list(range(300, 300 + 64 * 37, 37))),
-                         ("prefill", [512], [2048])], seed=61, device="cuda", fill="zero")
+                         ("prefill", [512], [2048])], seed=61, device="cuda")
     dec, pre = step.parts
+    host = HostInputs(step)
+    k0, v0 = step.k_pool.clone(), step.v_pool.clone()
     announce("mixed step: two streams vs one")
     gpu_store(step)
     d1 = gpu_part(step, dec)
     p1 = gpu_part(step, pre)
     torch.cuda.synchronize()
+    step.k_pool.copy_(k0)
+    step.v_pool.copy_(v0)
+    torch.cuda.synchronize()
     s1 = torch.cuda.current_stream()
     s2 = torch.cuda.Stream()
-    gpu_store(step)  # the same rows again: the pools do not change
+    gpu_store(step)
     stored = torch.cuda.Event()
     stored.record(s1)
     with torch.cuda.stream(s2):
@@ -556,6 +576,13 @@ def test_mixed_step_on_two_streams_matches_one_stream():
     p2 = gpu_part(step, pre)
     s1.wait_stream(s2)
     torch.cuda.synchronize()
+    assert np.array_equal(host_u16(step.k_pool), host.k_pool)
+    assert np.array_equal(host_u16(step.v_pool), host.v_pool)
+    ref_d, idx = oracle_decode(step, host, 0)
+    assert_close(host_u16(d2)[idx], ref_d, "two-stream decode")
+    windows = [(0, 0, 2048)]
+    ref_p, rows = oracle_prefill(step, host, 1, windows)
+    assert_close(host_u16(p2)[rows], ref_p, "two-stream prefill")
     assert torch.equal(d1, d2) and torch.equal(p1, p2)
 
 
@@ -610,3 +637,72 @@ def test_step_graph_replay_matches_eager():
         assert np.array_equal(host_u16(pout), ref_p), f"prefill differs on replay {r}"
         run()                      # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,lens", [
+    ("tiny_decode", None),                         # the one-launch path
+    ("split", [300, 1500, 40, 2048, 700, 64, 129]),  # split kernel + merge in the graph
+])
+def test_decode_store_graph_replay_matches_oracle(name, lens):
+    """The decode step as one pka_paged_attn_decode_store call captured in a HIP graph.
+    Before every replay the pools are put back to their state before the store (the new
+    tokens' slots NaN), so each replay must store the new rows itself; every replay's
+    pools must equal the oracle's store bit for bit and its output must match the
+    oracle. Eager work (the same call on other buffers) and synchronisation run between
+    the replays."""
+    import paged_kv_attention_25_amd as pka
+    if lens is None:
+        step = W.tiny_decode(device="cuda")
+    else:
+        step = W.build_step("graph_split", 16, 8, 16, 1024, [W.decode_spec(lens)], seed=78,
+                            device="cuda")
+    part = step.parts[0]
+    host = HostInputs(step)
+    k0, v0 = step.k_pool.clone(), step.v_pool.clone()
+    pt, seq, loc = dev_i32(part.page_table), dev_i32(part.seq_lens), dev_i32(step.out_loc)
+    ws = torch.zeros(max(1, pka.decode_workspace_bytes(step.num_q_heads, step.num_kv_heads,
+                                                       128, step.page_size, step.num_pages,
+                                                       part.batch, part.max_seq_len)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(part.q)
+    # eager work between replays: the same call on copies of the inputs
+    ek, ev = k0.clone(), v0.clone()
+    eout = torch.empty_like(part.q)
+    ews = torch.zeros_like(ws)
+
+    def run():
+        pka.paged_attn_decode_store(part.q, step.k_new, step.v_new, loc, step.k_pool,
+                                    step.v_pool, pt, seq, part.max_seq_len, step.page_size,
+                                    step.scale, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()                      # eager (loads the kernels before capture)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = host_u16(out).copy()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    ref, idx = oracle_decode(step, host, 0)
+    announce(f"decode_store graph replay ({name})")
+    for r in range(3):
+        step.k_pool.copy_(k0)
+        step.v_pool.copy_(v0)
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(step.k_pool), host.k_pool), f"k_pool, replay {r}"
+        assert np.array_equal(host_u16(step.v_pool), host.v_pool), f"v_pool, replay {r}"
+        got = host_u16(out)
+        assert np.array_equal(got, eager), f"replay {r} differs from the eager call"
+        assert_close(got[idx], ref, f"graph replay {r} ({name})")
+        ek.copy_(k0)
+        ev.copy_(v0)
+        pka.paged_attn_decode_store(part.q, step.k_new, step.v_new, loc, ek, ev, pt, seq,
+                                    part.max_seq_len, step.page_size, step.scale, out=eout,
+                                    workspace=ews)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(eout), eager)
