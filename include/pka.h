@@ -69,6 +69,8 @@ extern "C" {
 #define PKA_E_UNSUPPORTED (-3) /* valid, but not supported by these kernels */
 #define PKA_E_WORKSPACE (-4)   /* workspace missing or smaller than required */
 #define PKA_E_HIP (-5)         /* the HIP runtime reported an error */
+/* (-6 .. -8 are the scheduler's, in pka_sched.h) */
+#define PKA_E_SCRATCH (-9)     /* the call needs more than the static scratch holds */
 
 /* Pool and head geometry, shared by all calls.
  *   num_q_heads  Hq >= 1, a multiple of num_kv_heads
@@ -173,6 +175,32 @@ int pka_paged_attn_decode_store(const pka_geom* geom, const void* q, const void*
                                 int32_t page_table_stride, const int32_t* seq_lens,
                                 int32_t batch, int32_t max_seq_len, float scale, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pka_paged_attn_decode_store_noalloc - pka_paged_attn_decode_store without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The same launch and result as pka_paged_attn_decode_store (pools bit for bit, out
+ * identical); the split partials go to a static device array of the library instead
+ * of a caller workspace. Every argument is as in pka_paged_attn_decode_store.
+ *   Limit: the call's workspace need (pka_decode_workspace_bytes for the same geometry,
+ *          batch and max_seq_len) must be at most 16 MiB, else PKA_E_SCRATCH and nothing
+ *          is enqueued (e.g. Hq/Hkv = 16 at 1024 split wavefronts needs 16.9 MB).
+ *   Device: the array's address is looked up on the first call on a device (make that
+ *          call outside graph capture); the current device must be the stream's device
+ *          (else PKA_E_HIP). Each device holds its own copy until the process ends.
+ *   Sharing: every call on a device uses the same array, whose contents it overwrites
+ *          (they are never read before being written), so calls that overlap on one
+ *          device race; serialise them (one stream, or events between streams).
+ * The call allocates and frees nothing.
+ */
+int pka_paged_attn_decode_store_noalloc(const pka_geom* geom, const void* q, const void* k_new,
+                                        const void* v_new, const int32_t* out_loc, void* k_pool,
+                                        void* v_pool, const int32_t* page_table,
+                                        int32_t page_table_stride, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, float scale,
+                                        void* out, void* stream);
 
 /*
  * pka_paged_attn_prefill - causal extend prefill on top of a cached prefix.

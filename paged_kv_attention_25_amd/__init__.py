@@ -12,7 +12,8 @@ Functions (same names as the C entry points, without the ``pka_`` prefix):
   paged_attn_prefill(q, k_pool, v_pool, page_table, seq_lens, prefix_lens, extend_lens,
                      cu_extend, max_extend, max_seq_len, page_size, scale, out=None,
                      workspace=None)
-  paged_attn_decode_store(q, k_new, v_new, out_loc, ...)
+  paged_attn_decode_store(q, k_new, v_new, out_loc, ...), and its variant
+    paged_attn_decode_store_noalloc(...) that uses the library's static scratch
   decode_workspace_bytes(...), prefill_workspace_bytes(...)
 Tensor conventions: bf16 tensors may be torch.bfloat16 or int16/uint16 bit
 patterns; index tensors are int32; all tensors contiguous on the same GPU. Each call
@@ -40,6 +41,7 @@ PKA_E_SHAPE = -2
 PKA_E_UNSUPPORTED = -3
 PKA_E_WORKSPACE = -4
 PKA_E_HIP = -5
+PKA_E_SCRATCH = -9
 
 # Every symbol include/pka.h and include/pka_sched.h declare (the latter bound in
 # the `sched` submodule).
@@ -49,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "pka_store_kv",
     "pka_paged_attn_decode",
     "pka_paged_attn_decode_store",
+    "pka_paged_attn_decode_store_noalloc",
     "pka_decode_workspace_bytes",
     "pka_paged_attn_prefill",
     "pka_prefill_workspace_bytes",
@@ -107,6 +110,9 @@ def lib() -> ctypes.CDLL:
     L.pka_paged_attn_decode_store.restype = ctypes.c_int
     L.pka_paged_attn_decode_store.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                               f32, vp, vp, sz, vp]
+    L.pka_paged_attn_decode_store_noalloc.restype = ctypes.c_int
+    L.pka_paged_attn_decode_store_noalloc.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                      i32, i32, f32, vp, vp]
     L.pka_decode_workspace_bytes.restype = sz
     L.pka_decode_workspace_bytes.argtypes = [gp, i32, i32]
     L.pka_paged_attn_prefill.restype = ctypes.c_int
@@ -337,6 +343,31 @@ def paged_attn_decode_store(q, k_new, v_new, out_loc, k_pool, v_pool, page_table
                                              int(max_seq_len), float(scale), _ptr(out),
                                              _ptr(workspace), ws_bytes, _stream(q.device)),
            "pka_paged_attn_decode_store")
+    return out
+
+
+def paged_attn_decode_store_noalloc(q, k_new, v_new, out_loc, k_pool, v_pool, page_table,
+                                    seq_lens, max_seq_len, page_size, scale, out):
+    """pka_paged_attn_decode_store_noalloc: the same call as paged_attn_decode_store with
+    the split partials in the library's static device scratch; `out` [B, Hq, D] must be
+    given (nothing is allocated). Returns out."""
+    if out is None:
+        raise ValueError("out must be given: this call allocates nothing")
+    hkv, d, _ = _pools(k_pool, v_pool, page_size)
+    _tensor(q, "q", "bf16", (None, None, d))
+    extra = _new_rows(k_new, v_new, out_loc, int(q.shape[0]), hkv, d)
+    g, batch, named = _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out,
+                                     None, extra)
+    if _debug:
+        from . import checks
+        checks.check_decode_store(out_loc, seq_lens, int(max_seq_len), page_table,
+                                  int(page_size), g.num_pages)
+    _same_gpu(named)
+    _check(lib().pka_paged_attn_decode_store_noalloc(
+        ctypes.byref(g), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out_loc), _ptr(k_pool),
+        _ptr(v_pool), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch,
+        int(max_seq_len), float(scale), _ptr(out), _stream(q.device)),
+        "pka_paged_attn_decode_store_noalloc")
     return out
 
 

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG_DIR)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpka.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.cpp", "sched.cpp", "store_kv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "sched.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "scratch.hip"]
 # Per-source flags (none at present).
 SOURCE_FLAGS = {}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -47,6 +47,7 @@ const char* pka_status_string(int status) {
     case PKA_E_STATE: return "unknown request or wrong request state";
     case PKA_E_CAPACITY: return "output array or page-table row too small";
     case PKA_E_NOMEM: return "host memory allocation failed";
+    case PKA_E_SCRATCH: return "call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -83,7 +84,8 @@ size_t pka_decode_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t m
 namespace {
 
 // Checks and launch shared by the decode entry points; `store` non-null adds the
-// new tokens' store (k_new, v_new, out_loc) to the launch.
+// new tokens' store (k_new, v_new, out_loc) to the launch; `use_static` takes the
+// split partials' buffer from the library's static scratch instead of `workspace`.
 struct NewRows {
   const void* k_new;
   const void* v_new;
@@ -93,7 +95,8 @@ struct NewRows {
 int decode_impl(const pka_geom* geom, const void* q, const void* k_pool, const void* v_pool,
                 const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
                 int32_t batch, int32_t max_seq_len, float scale, void* out, void* workspace,
-                size_t workspace_bytes, void* stream, const NewRows* store) {
+                size_t workspace_bytes, void* stream, const NewRows* store,
+                bool use_static = false) {
   if (!geom) return PKA_E_NULLPTR;
   const int gs = attn_geom_status(geom);
   if (gs != PKA_OK) return gs;
@@ -110,6 +113,15 @@ int decode_impl(const pka_geom* geom, const void* q, const void* k_pool, const v
   const pka::DecodePlan plan = pka::plan_decode(batch, geom->num_kv_heads, group, max_seq_len);
   const size_t need =
       pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
+  if (use_static) {
+    if (need > pka::kStaticScratchBytes) return PKA_E_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      if (pka::static_scratch(as_stream(stream), &workspace) != hipSuccess) return PKA_E_HIP;
+      workspace_bytes = pka::kStaticScratchBytes;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKA_E_WORKSPACE;
   pka::DecodeArgs a;
   a.q = q;
@@ -159,6 +171,17 @@ int pka_paged_attn_decode_store(const pka_geom* geom, const void* q, const void*
   const NewRows rows{k_new, v_new, out_loc};
   return decode_impl(geom, q, k_pool, v_pool, page_table, page_table_stride, seq_lens, batch,
                      max_seq_len, scale, out, workspace, workspace_bytes, stream, &rows);
+}
+
+int pka_paged_attn_decode_store_noalloc(const pka_geom* geom, const void* q, const void* k_new,
+                                        const void* v_new, const int32_t* out_loc, void* k_pool,
+                                        void* v_pool, const int32_t* page_table,
+                                        int32_t page_table_stride, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, float scale,
+                                        void* out, void* stream) {
+  const NewRows rows{k_new, v_new, out_loc};
+  return decode_impl(geom, q, k_pool, v_pool, page_table, page_table_stride, seq_lens, batch,
+                     max_seq_len, scale, out, nullptr, 0, stream, &rows, true);
 }
 
 size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,

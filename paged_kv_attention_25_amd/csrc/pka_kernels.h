@@ -98,6 +98,12 @@ struct PrefillArgs {
 size_t prefill_workspace_bytes(int32_t batch, int32_t group, int32_t max_extend);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Static device scratch (scratch.hip) for the decode entry point that allocates
+// nothing: its address on the stream's device (which must be the current device),
+// looked up on the first call on that device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 inline int32_t page_shift_of(int32_t page_size) {
   if (page_size <= 0 || (page_size & (page_size - 1)) != 0) return -1;
   int32_t s = 0;

@@ -135,6 +135,31 @@ def test_decode_store_argument_errors(L):
     assert decode_store(L, geom(), batch=0, k_new=None) == pka.PKA_OK   # no-op
 
 
+def decode_store_noalloc(L, g, batch=4, max_seq=250, stride=256, k_new=FAKE, out=FAKE):
+    return L.pka_paged_attn_decode_store_noalloc(ctypes.byref(g) if g is not None else None,
+                                                 FAKE, k_new, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 stride, FAKE, batch, max_seq, 0.1, out, None)
+
+
+def test_decode_store_noalloc_argument_errors(L):
+    # the decode_store checks, then the static scratch's limit (16 MiB): none of these
+    # reaches the device
+    assert decode_store_noalloc(L, None) == pka.PKA_E_NULLPTR
+    assert decode_store_noalloc(L, geom(num_q_heads=12, num_kv_heads=8)) == pka.PKA_E_SHAPE
+    assert decode_store_noalloc(L, geom(head_dim=64)) == pka.PKA_E_UNSUPPORTED
+    assert decode_store_noalloc(L, geom(), stride=100, max_seq=250) == pka.PKA_E_SHAPE
+    assert decode_store_noalloc(L, geom(), k_new=None) == pka.PKA_E_NULLPTR
+    assert decode_store_noalloc(L, geom(), out=None) == pka.PKA_E_NULLPTR
+    # 16 q heads on one kv head: 1024 split wavefronts x 2 slots x 16 rows x 129 floats
+    g16 = geom(num_q_heads=16, num_kv_heads=1, num_pages=1 << 20)
+    need = L.pka_decode_workspace_bytes(ctypes.byref(g16), 64, 8192)
+    assert need > 16 << 20
+    assert decode_store_noalloc(L, g16, batch=64, max_seq=8192, stride=8192) == \
+        pka.PKA_E_SCRATCH
+    assert pka.status_string(pka.PKA_E_SCRATCH) != "unknown status"
+    assert decode_store_noalloc(L, geom(), batch=0, k_new=None) == pka.PKA_OK   # no-op
+
+
 def test_prefill_argument_errors(L):
     assert prefill(L, None) == pka.PKA_E_NULLPTR
     assert prefill(L, geom(head_dim=96)) == pka.PKA_E_UNSUPPORTED
