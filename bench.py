@@ -9,9 +9,9 @@ Prints ONE JSON line. The headline workload is the offline-style decode batch
 whole decode step of the path: the store of the 256 new tokens' K/V rows and the
 decode over all keys, made by pka_paged_attn_decode_store (the split decode kernel
 with the store inside, then its merge pass); the same step as store_kv followed by
-the decode call is timed beside it. `value` is the step's algorithmic HBM bytes
-(K+V of every attended token, q, out, page-table entries and seq_lens, plus the
-store's reads and writes) divided by the step's time, with inputs resident in
+the decode call is timed beside it. `value` is the decode's algorithmic HBM bytes
+(K+V of every attended token, q, out, page-table entries and seq_lens; the store's
+bytes are reported separately) divided by the step's time, with inputs resident in
 HBM and the caches flushed (a 1 GiB read) before every timed step.
 
 The other workloads (chunked prefill over cached prefixes, the tensor-parallel
@@ -24,8 +24,10 @@ Times come from HIP events recorded on the stream the kernels run on (torch's
 current stream, which the binding passes to every call): a step's time between one
 event before it and one after it; the per-call breakdown (store, decode, prefill) in a
 second pass with an event after every call. The oracle (float64,
-numpy, one BLAS thread) is timed on the host over the full decode batch as
-"cpu_baseline".
+numpy) is timed on the host over the full decode batch as "cpu_baseline" (one BLAS
+thread, and all the cores the process may use), on the chunked prefill as
+"prefill_cpu_baseline", and on every other workload (bounded samples) under each
+part's "oracle" record.
 """
 from __future__ import annotations
 
@@ -45,6 +47,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 METRIC = "decode attn HBM GB/s (% peak) + prefill attn TFLOP/s (% MFMA peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b256_traffic.json")
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_counters.json")
 
 
 def decode_bytes(part, step):
@@ -233,40 +236,165 @@ def two_stream_step_us(runner, steps, warmup, flush):
     return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
-def graph_step_us(runner, steps, flush):
-    """The whole step (store + every attention part) captured once as a HIP graph and
-    replayed: median µs per replay, caches flushed before each (launch overhead of the
-    separate calls is what the graph removes)."""
+def _host_u16(t):
+    return t.detach().cpu().contiguous().numpy().view(np.uint16)
+
+
+def _oracle_loop(fn, min_seconds, threads):
+    """Run fn() with `threads` BLAS threads until at least min_seconds have passed."""
+    from threadpoolctl import threadpool_limits
+    reps = 0
+    with threadpool_limits(threads):
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                return reps, el
+
+
+def step_part_view(part, idx):
+    """The requests `idx` of a decode part, as a part of their own (metadata only)."""
+    from paged_kv_attention_25_amd import workloads as W
+    return W.AttnPart(kind="decode", seq_lens=part.seq_lens[idx],
+                      prefix_lens=part.prefix_lens[idx], extend_lens=part.extend_lens[idx],
+                      cu_extend=np.arange(len(idx) + 1, dtype=np.int32),
+                      page_table=part.page_table[idx], q=None, row_offset=0)
+
+
+def oracle_for_part(name, step, min_seconds=2.0):
+    """The oracle timed on a bounded sample of one workload's attention calls, with as
+    many BLAS threads as the process may use. Decode samples are whole requests and are
+    charged the decode's algorithmic bytes; prefill samples are whole requests or a
+    window of tokens (an exact sub-problem) and are charged their algorithmic flops."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    kp, vp = _host_u16(step.k_pool), _host_u16(step.v_pool)
+    out = {}
+    for part in step.parts:
+        q = _host_u16(part.q)
+        if part.kind == "decode":
+            idx = np.arange(part.batch)
+            if name == "long_decode":
+                idx = idx[::8]                      # 4 of the 32 requests
+            sub = step_part_view(part, idx)
+            reps, el = _oracle_loop(
+                lambda: oracle.decode_ref(q[idx], kp, vp, sub.page_table, sub.seq_lens,
+                                          step.page_size, step.scale), min_seconds, cores)
+            nbytes = decode_bytes(sub, step)
+            out["decode"] = {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s",
+                             "cores": cores, "kind": "oracle",
+                             "us_per_call": round(el / reps * 1e6, 1),
+                             "sample": f"{len(idx)} of {part.batch} requests, {reps} pass(es) "
+                                       f"in {el:.1f} s, float64 numpy"}
+        else:
+            if name == "chunked_prefill":
+                bsel = np.arange(0, part.batch, 4)  # 8 of the 32 requests
+                wins = [(int(b), 0, int(part.extend_lens[b])) for b in bsel]
+                what = f"{len(bsel)} of {part.batch} requests (every 4th), all their rows"
+            else:
+                e = int(part.extend_lens[0])
+                wins = [(0, e - 1024, e)]           # the last 1024 tokens: the heaviest rows
+                what = "the chunk's last 1024 tokens (an exact sub-problem)"
+            rows = np.concatenate([np.arange(int(part.cu_extend[b]) + a,
+                                             int(part.cu_extend[b]) + c) for b, a, c in wins])
+            bidx = np.array([w[0] for w in wins])
+            pre = np.array([int(part.prefix_lens[b]) + a for b, a, c in wins])
+            ext = np.array([c - a for b, a, c in wins])
+            reps, el = _oracle_loop(
+                lambda: oracle.paged_attention_ref(q[rows], kp, vp, part.page_table[bidx],
+                                                   pre + ext, pre, ext, step.page_size,
+                                                   step.scale), min_seconds, cores)
+            flops = 4 * step.head_dim * step.num_q_heads * int((ext * pre +
+                                                                ext * (ext + 1) // 2).sum())
+            out["prefill"] = {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s",
+                              "cores": cores, "kind": "oracle",
+                              "sample": f"{what}, {reps} pass(es) in {el:.1f} s, float64 numpy, "
+                                        "same flop accounting as the GPU figure"}
+    return out
+
+
+QWEN3_06B_LAYERS = 28   # decoder layers of Qwen3-0.6B, the model whose heads tiny_decode has
+
+
+def graph_vs_eager(runner, steps, flush):
+    """The pages capture the decode step in a graph to cut CPU launch overhead. Times
+    the tiny decode step (one decode_store call) eagerly and as a replayed HIP graph:
+    GPU time per step with the host far ahead (events around the step, caches flushed
+    before it) and wall time per step back to back (the host issues step after step,
+    as a serving loop does). The same for a step over all 28 layers of the model (28
+    calls, each on its own layer's pools), eager against one graph of the 28 calls."""
     import torch
-    nparts = len(runner.step.parts)
+    s = runner.step
+    part = s.parts[0]
 
-    def step():
-        runner.store()
-        for i in range(nparts):
-            runner.attend(i)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(steps):
-        flush()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        graph.replay()
-        e1.record()
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
-    return float(np.median(ts))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def gpu_us(fn):
+        ts = []
+        for _ in range(steps):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def wall_us(fn, n=200):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / n
+
+    def one():
+        runner.attend(0)
+
+    g1 = capture(one)
+    # 28 layers: each layer's decode_store writes its own pools
+    pools = [(s.k_pool.clone(), s.v_pool.clone()) for _ in range(QWEN3_06B_LAYERS)]
+    m = runner.meta[0]
+    outs = [torch.empty_like(part.q) for _ in range(QWEN3_06B_LAYERS)]
+
+    def layers():
+        for (kp, vp), o in zip(pools, outs):
+            runner.pka.paged_attn_decode_store(part.q, s.k_new, s.v_new, runner.out_loc, kp, vp,
+                                               m["pt"], m["seq"], part.max_seq_len, s.page_size,
+                                               s.scale, out=o, workspace=m["ws"])
+
+    gl = capture(layers)
+    rec = {"graph_step_us": round(gpu_us(g1.replay), 2),
+           "back_to_back_wall_us_per_step": {"eager": round(wall_us(one), 2),
+                                             "graph": round(wall_us(g1.replay), 2)},
+           f"{QWEN3_06B_LAYERS}_layers": {
+               "gpu_us_per_step": {"eager": round(gpu_us(layers), 2),
+                                   "graph": round(gpu_us(gl.replay), 2)},
+               "back_to_back_wall_us_per_step": {"eager": round(wall_us(layers, 50), 2),
+                                                 "graph": round(wall_us(gl.replay, 50), 2)}},
+           "note": "gpu_us: events around one step with the host far ahead (after a cache "
+                   "flush); back_to_back_wall: host wall time per step over consecutive "
+                   "steps (the launch-overhead regime the graph is for)"}
+    del gl, g1, pools, outs
+    return rec
 
 
 def cpu_baseline(step, min_seconds=10.0):
@@ -280,7 +408,7 @@ def cpu_baseline(step, min_seconds=10.0):
     vp = step.v_pool.cpu().numpy().view(np.uint16)
     q = part.q.cpu().numpy().view(np.uint16)
 
-    def timed(threads):
+    def timed(threads, seconds=min_seconds):
         reps = 0
         with threadpool_limits(threads):
             t0 = time.perf_counter()
@@ -289,13 +417,13 @@ def cpu_baseline(step, min_seconds=10.0):
                                   step.scale)
                 reps += 1
                 el = time.perf_counter() - t0
-                if el >= min_seconds:
+                if el >= seconds:
                     break
         return decode_bytes(part, step) * reps / el / 1e9, reps, el
 
     gbs, reps, el = timed(1)
     cores = len(os.sched_getaffinity(0))
-    gbs_n, reps_n, el_n = timed(cores)
+    gbs_n, reps_n, el_n = timed(cores, min_seconds / 2)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full decode_b256 batch (256 requests), {reps} pass(es) in {el:.1f} s, "
                       "float64 numpy, one BLAS thread, same byte accounting as value",
@@ -303,6 +431,16 @@ def cpu_baseline(step, min_seconds=10.0):
                           "sample": f"the same, {reps_n} pass(es) in {el_n:.1f} s, "
                                     f"{cores} BLAS threads (the oracle's per-request, "
                                     "per-head products are small, so threads add little)"}}
+
+
+def prefill_counters_for(kernel_hash):
+    if not os.path.exists(PREFILL_COUNTERS_FILE):
+        return None
+    with open(PREFILL_COUNTERS_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_hash:
+        return None
+    return rec.get("workloads")
 
 
 def traffic_for(kernel_hash):
@@ -381,6 +519,86 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+def _dispatch_rows(csv_dir, counters):
+    """Per-dispatch counter values and durations from rocprofv3 counter CSVs:
+    {kernel name: [{counter: value, ..., "ns": duration}, ...]}."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] not in counters:
+                    continue
+                key = (r["Kernel_Name"], fn, r["Dispatch_Id"])
+                d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                         "grid": int(r["Grid_Size"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _, _), d in per.items():
+        out.setdefault(name, []).append(d)
+    return out
+
+
+def write_prefill_counters(workload, busy_dir, fetch_dir, write_dir):
+    """MFMA busy fraction, shader clock and HBM bytes per prefill launch of one workload
+    from three rocprofv3 counter runs of `bench.py --part W --calibration-copy`
+    (SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE, then FETCH_SIZE, then WRITE_SIZE); the
+    byte counters are scaled by what they read for the 512 MiB copy in the same run."""
+    busy = _dispatch_rows(busy_dir, ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+    fetch = _dispatch_rows(fetch_dir, ("FETCH_SIZE",))
+    write = _dispatch_rows(write_dir, ("WRITE_SIZE",))
+
+    def rows(d, tag, largest_grid=False):
+        vals = [v for name, vs in d.items() if tag in name for v in vs]
+        if largest_grid and vals:
+            g = max(v["grid"] for v in vals)
+            vals = [v for v in vals if v["grid"] == g]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named *{tag}*")
+        return vals
+
+    b = [r for r in rows(busy, "prefill_kernel")]
+    xcds = 8       # GRBM_GUI_ACTIVE is summed over the XCDs
+    simds = 1024   # 256 CUs x 4 SIMDs
+    active = np.mean([r["GRBM_GUI_ACTIVE"] / xcds for r in b])
+    mfma = np.mean([r["SQ_VALU_MFMA_BUSY_CYCLES"] for r in b])
+    ns = np.mean([r["ns"] for r in b])
+    kib = 1024.0
+    fscale = COPY_BYTES / (np.mean([r["FETCH_SIZE"] for r in rows(fetch, "copyBuffer", True)]) * kib)
+    wscale = COPY_BYTES / (np.mean([r["WRITE_SIZE"] for r in rows(write, "copyBuffer", True)]) * kib)
+    rd = np.mean([r["FETCH_SIZE"] for r in rows(fetch, "prefill_kernel")]) * kib * fscale
+    wr = np.mean([r["WRITE_SIZE"] for r in rows(write, "prefill_kernel")]) * kib * wscale
+    h = source_hash("prefill.hip", "pka_device.h")
+    rec = {"source_hash": h, "workloads": {}}
+    if os.path.exists(PREFILL_COUNTERS_FILE):
+        with open(PREFILL_COUNTERS_FILE) as f:
+            old = json.load(f)
+        if old.get("source_hash") == h:
+            rec = old
+    rec["workloads"][workload] = {
+        "mfma_busy": round(float(mfma / (active * simds)), 4),
+        "shader_clock_ghz": round(float(active / ns), 3),
+        "duration_us_under_counters": round(float(ns / 1e3), 1),
+        "hbm_bytes": int(round(rd + wr)), "hbm_read_bytes": int(round(rd)),
+        "hbm_write_bytes": int(round(wr)),
+        "fetch_scale": round(float(fscale), 4), "write_scale": round(float(wscale), 4),
+        "dispatches": len(b)}
+    rec["commands"] = [
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d <busy_dir> "
+        "--output-format csv -- python3 bench.py --part W --steps 3 --warmup 1 "
+        "--no-cpu-baseline --calibration-copy",
+        "rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- (same command)",
+        "rocprofv3 --pmc WRITE_SIZE -d <write_dir> --output-format csv -- (same command)",
+        "python3 bench.py --prefill-counters-from W <busy_dir> <fetch_dir> <write_dir>"]
+    with open(PREFILL_COUNTERS_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def calibration_copy(flush):
     """Two plain device copies of COPY_BYTES: the reference for the traffic counters."""
     import torch
@@ -398,8 +616,9 @@ def calibration_copy(flush):
 PART_NAMES = ("long_decode", "tiny_decode", "chunked_prefill", "tp4_mixed")
 
 
-def time_part(name, steps, warmup, flush, log):
-    """Time one of the non-headline workloads; per-segment medians in its record."""
+def time_part(name, steps, warmup, flush, log, cpu=True):
+    """Time one of the non-headline workloads; per-segment medians in its record; with
+    `cpu`, the oracle on a bounded sample of the same inputs under "oracle"."""
     import torch
     from paged_kv_attention_25_amd import workloads as W
     log(f"{name}: generating inputs")
@@ -426,12 +645,17 @@ def time_part(name, steps, warmup, flush, log):
         # a fused step is its one decode call: its time is the step's (no event inside)
         us = tot * 1e3 if r.fused else seg[i + 1] * 1e3
         if p.kind == "decode":
-            # the fused launch also moves the store's bytes
-            nbytes = decode_bytes(p, st) + (store_bytes(st) if r.fused else 0)
+            # decode bytes only; a fused launch's store is reported beside them
+            nbytes = decode_bytes(p, st)
             gbs = nbytes / (us * 1e-6) / 1e9
             rec["decode_us"] = round(us, 2)
             rec["decode_GBs"] = round(gbs, 1)
             rec["decode_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+            rec["decode_bytes"] = nbytes
+            if r.fused:
+                rec["store_bytes_in_call"] = store_bytes(st)
+                rec["call_GBs_incl_store"] = round((nbytes + store_bytes(st)) /
+                                                   (us * 1e-6) / 1e9, 1)
             rec["decode_TFLOPs_context"] = round(decode_flops(p, st) / (us * 1e-6) / 1e12, 2)
         else:
             tf = prefill_flops(p, st) / (us * 1e-6) / 1e12
@@ -443,11 +667,14 @@ def time_part(name, steps, warmup, flush, log):
     if r.fused:
         rec["unfused_step_us"] = round(tot_u * 1e3, 2)   # store_kv, then decode
     if name == "tiny_decode":
-        rec["graph_step_us"] = round(graph_step_us(r, steps, flush), 2)
+        rec.update(graph_vs_eager(r, steps, flush))
     kinds = {p.kind for p in st.parts}
     if kinds == {"decode", "prefill"}:
         # the same step with the decode beside the prefill on a second stream
         rec["two_stream_step_us"] = round(two_stream_step_us(r, steps, 10, flush), 2)
+    if cpu:
+        log(f"{name}: oracle on a sample")
+        rec["oracle"] = oracle_for_part(name, st)
     log(f"{name}: {rec}")
     del r, st
     torch.cuda.empty_cache()
@@ -589,12 +816,19 @@ def main():
                     help="also run two 512 MiB device copies (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the decode_b256 traffic record from two counter runs, then exit")
+    ap.add_argument("--prefill-counters-from", nargs=4,
+                    metavar=("WORKLOAD", "BUSY_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the prefill counter record of one workload from three counter "
+                         "runs, then exit")
     ap.add_argument("--part", choices=PART_NAMES,
                     help="time only this workload (its warmup is --warmup), print its record, "
                          "exit (for profiling one workload)")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
+        return
+    if args.prefill_counters_from:
+        write_prefill_counters(*args.prefill_counters_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the attention path here runs on one GPU only; --gpus must "
@@ -623,7 +857,8 @@ def main():
         if args.calibration_copy:
             calibration_copy(flush)
         print(json.dumps({"part": args.part,
-                          **time_part(args.part, args.steps, args.warmup, flush, log)}),
+                          **time_part(args.part, args.steps, args.warmup, flush, log,
+                                      cpu=not args.no_cpu_baseline)}),
               flush=True)
         return
 
@@ -636,9 +871,9 @@ def main():
     seg, total_ms, wall = time_step(run, args.steps, args.warmup, flush)
     dec_bytes = decode_bytes(part, step)
     st_bytes = store_bytes(step)
-    value = (dec_bytes + st_bytes) / (total_ms * 1e-3) / 1e9
-    # the launch stores and decodes: its algorithmic bytes are both
-    launch_bytes = dec_bytes + st_bytes
+    # decode bytes only (the store inside the same launch is reported beside them)
+    value = dec_bytes / (total_ms * 1e-3) / 1e9
+    launch_bytes = dec_bytes
     launch_ms = total_ms   # the step is the one decode_store call (split + merge)
     dec_gbs = launch_bytes / (launch_ms * 1e-3) / 1e9
     log(f"decode_b256: step {total_ms*1e3:.1f} us; {dec_gbs:.0f} GB/s")
@@ -648,7 +883,10 @@ def main():
                 "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(khash),
                 "algorithmic_bytes_per_launch": launch_bytes,
-                "avg_launch_us": round(launch_ms * 1e3, 2)}
+                "store_bytes_per_launch_not_counted": st_bytes,
+                "avg_launch_us": round(launch_ms * 1e3, 2),
+                "launch": "one pka_paged_attn_decode_store call (split kernel with the store "
+                          "inside, then the merge kernel), timed with HIP events on its stream"}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 4),
@@ -659,6 +897,9 @@ def main():
                                "step = decode_store (split decode with the store of the 256 "
                                "new rows inside) + merge",
                    "batch": part.batch, "sum_context": int(part.seq_lens.sum()),
+                   "decode_bytes_per_step": dec_bytes, "store_bytes_per_step": st_bytes,
+                   "step_GBs_incl_store": round((dec_bytes + st_bytes) / (total_ms * 1e-3) / 1e9,
+                                                1),
                    "decode_TFLOPs_context": round(decode_flops(part, step) /
                                                   (total_ms * 1e-3) / 1e12, 2),
                    "timing": "HIP events on the launch stream, caches flushed before each step; "
@@ -677,7 +918,7 @@ def main():
         seg_u, tot_u, _ = time_step(run_u, args.steps, args.warmup, flush)
         result["config"]["unfused_step"] = {
             "step_us": round(tot_u * 1e3, 2),
-            "value_GBs": round((dec_bytes + st_bytes) / (tot_u * 1e-3) / 1e9, 1),
+            "value_GBs": round(dec_bytes / (tot_u * 1e-3) / 1e9, 1),
             "with_an_event_after_each_call": {"store_us": round(seg_u[0] * 1e3, 2),
                                               "decode_us": round(seg_u[1] * 1e3, 2)}}
         del run_u
@@ -693,7 +934,8 @@ def main():
     parts = {}
     if not args.quick:
         for name in PART_NAMES:
-            parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log)
+            parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log,
+                                    cpu=not args.no_cpu_baseline)
         parts["host_sched"] = host_sched_bench(log)
         parts["page_sizes"] = page_size_sweep(args.steps, args.warmup, flush, log)
         cp = parts["chunked_prefill"]
@@ -701,6 +943,21 @@ def main():
                                          "prefixes U[0,4096], 8192 new tokens, page_size 16",
                              "value": cp["prefill_TFLOPs"], "unit": "TFLOP/s",
                              "peak": MFMA_BF16_PEAK_TFLOPS, "frac": cp["prefill_frac_mfma"]}
+        counters = prefill_counters_for(source_hash("prefill.hip", "pka_device.h"))
+        cw = (counters or {}).get("chunked_prefill", {})
+        result["prefill_roofline"] = {
+            "bound": "mfma", "kernel": "prefill_plan_kernel + prefill_kernel",
+            "achieved": cp["prefill_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": cp["prefill_frac_mfma"],
+            "algorithmic_flops_per_launch": cp["prefill_flops"],
+            "avg_launch_us": cp["prefill_us"],
+            "launch": "one pka_paged_attn_prefill call, timed with HIP events on its stream",
+            "mfma_busy": cw.get("mfma_busy"), "shader_clock_ghz": cw.get("shader_clock_ghz"),
+            "traffic": cw.get("hbm_bytes"),
+            "counters": "profiles/prefill_counters.json (rocprofv3 on the same source), or "
+                        "null when the kernel changed since they were taken"}
+        if "oracle" in cp:
+            result["prefill_cpu_baseline"] = cp["oracle"]["prefill"]
     result["parts"] = parts
     print(json.dumps(result), flush=True)
 

@@ -166,23 +166,42 @@ def make_geom(num_q_heads, num_kv_heads, head_dim, page_size, num_pages) -> Geom
 
 # --- host-side tensor checks ------------------------------------------------------------
 
+_torch_types = None
+
+
+def _types():
+    """(torch.Tensor, the bf16-carrying dtypes, torch.int32), looked up once."""
+    global _torch_types
+    if _torch_types is None:
+        import torch
+        _torch_types = (torch.Tensor, (torch.bfloat16, torch.int16, torch.uint16), torch.int32)
+    return _torch_types
+
+
 def _tensor(t, name, kind, shape):
     """`t` must be a contiguous torch tensor of `kind` ("bf16": bfloat16 or 16-bit
     integer bit patterns; "i32"; "bytes": any dtype) whose shape matches `shape`
     (None entries match any size)."""
-    import torch
-    if not isinstance(t, torch.Tensor):
+    tensor_t, bf16_dtypes, i32 = _types()
+    if not isinstance(t, tensor_t):
         raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
-    if kind == "bf16" and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise ValueError(f"{name} must hold bf16 values (torch.bfloat16 or 16-bit bit "
-                         f"patterns), got {t.dtype}")
-    if kind == "i32" and t.dtype != torch.int32:
+    if kind == "bf16":
+        if t.dtype not in bf16_dtypes:
+            raise ValueError(f"{name} must hold bf16 values (torch.bfloat16 or 16-bit bit "
+                             f"patterns), got {t.dtype}")
+    elif kind == "i32" and t.dtype != i32:
         raise ValueError(f"{name} must be int32, got {t.dtype}")
     if shape is not None:
-        if t.dim() != len(shape) or any(w is not None and int(s) != int(w)
-                                        for s, w in zip(t.shape, shape)):
+        got = t.shape
+        bad = len(got) != len(shape)
+        if not bad:
+            for have, want in zip(got, shape):
+                if want is not None and have != want:
+                    bad = True
+                    break
+        if bad:
             want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
-            raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+            raise ValueError(f"{name} has shape {list(got)}, expected {want}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -193,12 +212,13 @@ def _same_gpu(named):
     for name, t in named.items():
         if t is None:
             continue
-        if t.device.type != "cuda":
+        if not t.is_cuda:
             raise ValueError(f"{name} is on {t.device}; every tensor must be on the GPU")
+        d = t.get_device()
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
-            raise ValueError(f"{name} is on {t.device}, other tensors on {dev}")
+            dev = d
+        elif d != dev:
+            raise ValueError(f"{name} is on cuda:{d}, other tensors on cuda:{dev}")
     return dev
 
 
@@ -265,11 +285,15 @@ def _alloc_like(q, nbytes):
 
 
 def _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out, workspace,
-                   extra=None):
-    """Checks shared by the decode entry points; returns (geometry, batch, the tensors
-    by name for the device check)."""
-    hkv, d, num_pages = _pools(k_pool, v_pool, page_size)
-    _tensor(q, "q", "bf16", (None, None, d))
+                   extra=None, pools=None):
+    """Checks shared by the decode entry points (`pools`: _pools' result when the caller
+    has checked the pools and q already); returns (geometry, batch, the tensors by name
+    for the device check)."""
+    if pools is None:
+        hkv, d, num_pages = _pools(k_pool, v_pool, page_size)
+        _tensor(q, "q", "bf16", (None, None, d))
+    else:
+        hkv, d, num_pages = pools
     batch, hq = int(q.shape[0]), int(q.shape[1])
     if hq % hkv:
         raise ValueError(f"q has {hq} heads, not a multiple of the pools' {hkv} kv heads")
@@ -320,11 +344,12 @@ def paged_attn_decode_store(q, k_new, v_new, out_loc, k_pool, v_pool, page_table
     out_loc[b] of the pools and decodes, in one launch (the same result as store_kv then
     paged_attn_decode). Returns out [B, Hq, D]."""
     import torch
-    hkv, d, _ = _pools(k_pool, v_pool, page_size)
+    pools = _pools(k_pool, v_pool, page_size)
+    hkv, d, _ = pools
     _tensor(q, "q", "bf16", (None, None, d))
     extra = _new_rows(k_new, v_new, out_loc, int(q.shape[0]), hkv, d)
     g, batch, named = _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out,
-                                     workspace, extra)
+                                     workspace, extra, pools)
     if _debug:
         from . import checks
         checks.check_decode_store(out_loc, seq_lens, int(max_seq_len), page_table,
@@ -353,11 +378,12 @@ def paged_attn_decode_store_noalloc(q, k_new, v_new, out_loc, k_pool, v_pool, pa
     given (nothing is allocated). Returns out."""
     if out is None:
         raise ValueError("out must be given: this call allocates nothing")
-    hkv, d, _ = _pools(k_pool, v_pool, page_size)
+    pools = _pools(k_pool, v_pool, page_size)
+    hkv, d, _ = pools
     _tensor(q, "q", "bf16", (None, None, d))
     extra = _new_rows(k_new, v_new, out_loc, int(q.shape[0]), hkv, d)
     g, batch, named = _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out,
-                                     None, extra)
+                                     None, extra, pools)
     if _debug:
         from . import checks
         checks.check_decode_store(out_loc, seq_lens, int(max_seq_len), page_table,
