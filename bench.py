@@ -152,9 +152,14 @@ class Runner:
 
 
 PART_WARMUP = 60  # warmup steps of the workloads reported under "parts"
+# ... and at least this much continuous work before their timing: under sustained
+# matrix-core load the shader clock settles only after a few hundred ms (the prefill
+# ran 301 us on its first timed pass after 300 calls and 268-269 us from then on, on
+# one box), and a serving step runs at that steady state.
+PART_WARM_SECONDS = 0.5
 
 
-def time_step(runner, steps, warmup, flush, cold=True):
+def time_step(runner, steps, warmup, flush, cold=True, warm_seconds=0.0):
     """Run warmup steps, then time `steps` steps twice. Pass 1 records one HIP event
     before and one after each step (the step's time: an event marker between calls
     holds the stream for a few µs, so none is placed inside the step). Pass 2 records
@@ -173,6 +178,11 @@ def time_step(runner, steps, warmup, flush, cold=True):
     for _ in range(warmup):
         calls()
     torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < warm_seconds:
+        for _ in range(20):
+            calls()
+        torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
@@ -625,7 +635,7 @@ def time_part(name, steps, warmup, flush, log, cpu=True):
     st = W.WORKLOADS[name](device="cuda", fill="zero")
     r = Runner(st, fused=True)
     torch.cuda.synchronize()
-    seg, tot, _ = time_step(r, steps, warmup, flush)
+    seg, tot, _ = time_step(r, steps, warmup, flush, warm_seconds=PART_WARM_SECONDS)
     if r.fused:
         # The fused step and store_kv + decode, timed alternately (a second time each)
         # so that neither gains from the order; each reports the mean of its two medians.
@@ -705,7 +715,8 @@ def page_size_sweep(steps, warmup, flush, log):
         st = W.chunked_prefill(device="cuda", fill="zero", page_size=P)
         r = Runner(st)
         torch.cuda.synchronize()
-        seg, _, _ = time_step(r, steps, max(warmup, PART_WARMUP), flush)
+        seg, _, _ = time_step(r, steps, max(warmup, PART_WARMUP), flush,
+                              warm_seconds=PART_WARM_SECONDS)
         us = seg[1] * 1e3
         tf = prefill_flops(st.parts[0], st) / (us * 1e-6) / 1e12
         out["chunked_prefill"][f"P{P}"] = {"prefill_us": round(us, 2),

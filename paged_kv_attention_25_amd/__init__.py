@@ -280,8 +280,9 @@ def prefill_workspace_bytes(num_q_heads, num_kv_heads, head_dim, page_size, num_
 
 
 def _alloc_like(q, nbytes):
+    """A workspace for one call, zeroed (the decode's work counters start at zero)."""
     import torch
-    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=q.device)
+    return torch.zeros(max(1, int(nbytes)), dtype=torch.uint8, device=q.device)
 
 
 def _decode_inputs(q, k_pool, v_pool, page_table, seq_lens, page_size, out, workspace,
