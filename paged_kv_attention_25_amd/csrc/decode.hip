@@ -659,9 +659,8 @@ __device__ __forceinline__ void merge_one_round(const float* __restrict__ part_o
 constexpr int kMergeWaves = 4;
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ req_blocks,
-    uint16_t* __restrict__ out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t max_seq_len, int32_t groups) {
+    const int32_t* __restrict__ req_blocks, uint16_t* __restrict__ out, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t groups) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (row >= (int64_t)batch * num_q_heads) return;
@@ -670,11 +669,13 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
   const int G = num_q_heads / num_kv_heads;
   const int g = h / G;
   const int nq = h - g * G;
-  const int32_t nb = blocks_of(min(seq_lens[b], max_seq_len));
-  if (nb == 0) return;
-  const int32_t nb_head = req_blocks[batch];
-  groups = min(groups, nb_head);  // as in the split kernel
+  // The pair's blocks from the prefix sums alone (they count min(seq_len, max_seq_len)),
+  // so that its three loads go out together.
   const int32_t S = req_blocks[b];
+  const int32_t nb = req_blocks[b + 1] - S;
+  const int32_t nb_head = req_blocks[batch];
+  if (nb <= 0) return;
+  groups = min(groups, nb_head);  // as in the split kernel
   const int32_t c0 = group_of(S, nb_head, groups);
   const int32_t c1 = group_of(S + nb - 1, nb_head, groups);
   if (c0 == c1) return;  // written directly by the split kernel
@@ -815,8 +816,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   hipLaunchKernelGGL(decode_merge_kernel,
                      dim3((unsigned)((merge_rows + kMergeWaves - 1) / kMergeWaves)),
                      dim3(64 * kMergeWaves), 0, stream,
-                     k.part_o, k.part_lse, a.seq_lens, k.req_blocks, (uint16_t*)a.out, a.batch,
-                     a.num_q_heads, a.num_kv_heads, a.max_seq_len, plan.groups);
+                     k.part_o, k.part_lse, k.req_blocks, (uint16_t*)a.out, a.batch,
+                     a.num_q_heads, a.num_kv_heads, plan.groups);
   return hipGetLastError();
 }
 
