@@ -263,21 +263,6 @@ void prefill_kernel(PrefillKernelArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kStages * kTileElems];
   __shared__ __attribute__((aligned(16))) int32_t ids_lds[kStages][kLoaders][64];
 
-  // Q^T operands: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
-  u32x4 qv[8];
-  if (row_ok) {
-    const u32x4* src = (const u32x4*)(p.q + ((int64_t)(q_row0 + tok) * p.num_q_heads +
-                                              (int64_t)g * G + hh) * kHeadDim + 8 * hgrp);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qv[c] = src[2 * c];
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qv[c] = u32x4{0, 0, 0, 0};
-  }
-  // Q has landed before any copy into LDS is issued: the compiler does not see those
-  // copies, so a wait it placed for Q later on would also wait for them.
-  wait_vmcnt<0>();
-
   // K/V tiles go from the pool straight into LDS (no registers in between). Only the
   // first kLoaders wavefronts load (they get issue priority on their SIMDs and so have
   // slack before each barrier); loader w loads keys 16w .. 16w+15 of a tile:
@@ -364,15 +349,34 @@ void prefill_kernel(PrefillKernelArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t4][i] = 0.f;
 
-  // Prologue (loaders): page-table entries of tiles 0..4 and the K/V of tiles 0..2.
+  // Prologue. The loaders' copies of the page-table entries of tiles 0..3 go out
+  // together with Q's loads, and one wait covers both.
   if (loader) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) ids_dma(t * kKeysPerTile, t);
-    wait_vmcnt<0>();
+  }
+  // Q^T operands: 8 MFMAs over D, lane feeds d = 16c + 8*hgrp .. +8 of its row.
+  u32x4 qv[8];
+  if (row_ok) {
+    const u32x4* src = (const u32x4*)(p.q + ((int64_t)(q_row0 + tok) * p.num_q_heads +
+                                              (int64_t)g * G + hh) * kHeadDim + 8 * hgrp);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[c] = src[2 * c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[c] = u32x4{0, 0, 0, 0};
+  }
+  // Q has landed before any tile copy is issued: the compiler does not see those
+  // copies, so a wait it placed for Q after them would also wait for them.
+  wait_vmcnt<0>();
+  // Then the K/V of tiles 0..2 and the entries of tile 4 (ring slot 0: tile 0's entries
+  // have been read by then). Only tile 0 (the first 8 of these 25 copies) has landed
+  // before the first barrier; the loop's first wait covers the rest.
+  if (loader) {
 #pragma unroll
     for (int t = 0; t < 3; ++t) dma_tile(t * kKeysPerTile, t, t);
-    ids_dma(4 * kKeysPerTile, 0);  // ring slot 0: tile 0's entries were read above
-    wait_vmcnt<0>();
+    ids_dma(4 * kKeysPerTile, 0);
+    wait_vmcnt<17>();
   }
   lds_barrier();
 
