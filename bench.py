@@ -626,7 +626,7 @@ def calibration_copy(flush):
 PART_NAMES = ("long_decode", "tiny_decode", "chunked_prefill", "tp4_mixed")
 
 
-def time_part(name, steps, warmup, flush, log, cpu=True):
+def time_part(name, steps, warmup, flush, log, cpu=True, warm_seconds=PART_WARM_SECONDS):
     """Time one of the non-headline workloads; per-segment medians in its record; with
     `cpu`, the oracle on a bounded sample of the same inputs under "oracle"."""
     import torch
@@ -635,7 +635,7 @@ def time_part(name, steps, warmup, flush, log, cpu=True):
     st = W.WORKLOADS[name](device="cuda", fill="zero")
     r = Runner(st, fused=True)
     torch.cuda.synchronize()
-    seg, tot, _ = time_step(r, steps, warmup, flush, warm_seconds=PART_WARM_SECONDS)
+    seg, tot, _ = time_step(r, steps, warmup, flush, warm_seconds=warm_seconds)
     if r.fused:
         # The fused step and store_kv + decode, timed alternately (a second time each)
         # so that neither gains from the order; each reports the mean of its two medians.
@@ -694,7 +694,7 @@ def time_part(name, steps, warmup, flush, log, cpu=True):
 PAGE_SIZES = (1, 16, 32, 64)
 
 
-def page_size_sweep(steps, warmup, flush, log):
+def page_size_sweep(steps, warmup, flush, log, warm_seconds=PART_WARM_SECONDS):
     """decode_b256 (the decode_store step) and chunked_prefill with the pool cut into
     pages of 1, 16, 32 and 64 slots: the same requests, pages drawn at random. The
     kernels take any page size at run time (powers of two by shift and mask)."""
@@ -705,8 +705,8 @@ def page_size_sweep(steps, warmup, flush, log):
         st = W.decode_b256(device="cuda", fill="zero", page_size=P)
         r = Runner(st, fused=True)
         torch.cuda.synchronize()
-        _, tot, _ = time_step(r, steps, warmup, flush)
-        nbytes = decode_bytes(st.parts[0], st) + store_bytes(st)
+        _, tot, _ = time_step(r, steps, warmup, flush, warm_seconds=warm_seconds)
+        nbytes = decode_bytes(st.parts[0], st)   # decode bytes only, as the headline
         out["decode_b256"][f"P{P}"] = {"step_us": round(tot * 1e3, 2),
                                        "GBs": round(nbytes / (tot * 1e-3) / 1e9, 1)}
         del r, st
@@ -716,7 +716,7 @@ def page_size_sweep(steps, warmup, flush, log):
         r = Runner(st)
         torch.cuda.synchronize()
         seg, _, _ = time_step(r, steps, max(warmup, PART_WARMUP), flush,
-                              warm_seconds=PART_WARM_SECONDS)
+                              warm_seconds=warm_seconds)
         us = seg[1] * 1e3
         tf = prefill_flops(st.parts[0], st) / (us * 1e-6) / 1e12
         out["chunked_prefill"][f"P{P}"] = {"prefill_us": round(us, 2),
@@ -831,6 +831,9 @@ def main():
                     metavar=("WORKLOAD", "BUSY_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the prefill counter record of one workload from three counter "
                          "runs, then exit")
+    ap.add_argument("--warm-seconds", type=float, default=PART_WARM_SECONDS,
+                    help="continuous work before each timing (default %(default)s s; counter "
+                         "runs that need no steady clock can pass 0)")
     ap.add_argument("--part", choices=PART_NAMES,
                     help="time only this workload (its warmup is --warmup), print its record, "
                          "exit (for profiling one workload)")
@@ -869,6 +872,7 @@ def main():
             calibration_copy(flush)
         print(json.dumps({"part": args.part,
                           **time_part(args.part, args.steps, args.warmup, flush, log,
+                                      warm_seconds=args.warm_seconds,
                                       cpu=not args.no_cpu_baseline)}),
               flush=True)
         return
@@ -879,7 +883,8 @@ def main():
     run = Runner(step, fused=True)
     part = step.parts[0]
     torch.cuda.synchronize()
-    seg, total_ms, wall = time_step(run, args.steps, args.warmup, flush)
+    seg, total_ms, wall = time_step(run, args.steps, args.warmup, flush,
+                                    warm_seconds=args.warm_seconds)
     dec_bytes = decode_bytes(part, step)
     st_bytes = store_bytes(step)
     # decode bytes only (the store inside the same launch is reported beside them)
@@ -914,7 +919,8 @@ def main():
                    "decode_TFLOPs_context": round(decode_flops(part, step) /
                                                   (total_ms * 1e-3) / 1e12, 2),
                    "timing": "HIP events on the launch stream, caches flushed before each step; "
-                             "median over the timed steps",
+                             "median over the timed steps, after half a second of continuous "
+                             "steps",
                    "wall_s_timed_region_incl_flush": round(wall, 4)},
         "roofline": roofline,
     }
@@ -946,9 +952,11 @@ def main():
     if not args.quick:
         for name in PART_NAMES:
             parts[name] = time_part(name, args.steps, max(args.warmup, PART_WARMUP), flush, log,
-                                    cpu=not args.no_cpu_baseline)
+                                    cpu=not args.no_cpu_baseline,
+                                    warm_seconds=args.warm_seconds)
         parts["host_sched"] = host_sched_bench(log)
-        parts["page_sizes"] = page_size_sweep(args.steps, args.warmup, flush, log)
+        parts["page_sizes"] = page_size_sweep(args.steps, args.warmup, flush, log,
+                                              warm_seconds=args.warm_seconds)
         cp = parts["chunked_prefill"]
         result["prefill"] = {"workload": "chunked_prefill: Qwen3-14B heads 40q/8kv, 32 requests, "
                                          "prefixes U[0,4096], 8192 new tokens, page_size 16",
