@@ -548,13 +548,57 @@ void decode_small_kernel(DecodeKernelArgs p) {
   const int grp = lane >> 4;
   const int32_t b = uniform((int32_t)blockIdx.x / p.num_kv_heads);
   const int32_t g = uniform((int32_t)blockIdx.x - b * p.num_kv_heads);
-  const int32_t L = uniform(min(p.seq_lens[b], p.max_seq_len));
-  if (L <= 0) return;  // no keys: the output row is not written (as in the split path)
+  // The page-table entry of key k0 + lane (and, for the store, the request's out_loc
+  // and new rows) load together with the request's length, as none of them depends on
+  // it: the block's keys past the length are redirected to key L - 1 afterwards. The
+  // kernel arguments these loads need are in registers first, so that no wait for one
+  // of those arguments also waits for a load already in flight.
+  const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_stride;
+  const int32_t* len_at = p.seq_lens + b;
+  const int32_t* loc_at = p.out_loc + b;
+  asm volatile("" ::"s"(pt_row), "s"(len_at), "s"(loc_at), "s"(p.pg.page_shift),
+               "s"(p.pg.page_size), "s"(p.pg.table_width), "s"(p.pg.div_magic),
+               "s"(p.pg.div_shift), "s"(p.max_seq_len));
   Desc d;
   d.b = b;
   d.g = g;
-  d.L = L;
   d.k0 = wave * kBlock;
+  RawSlot raw;
+  raw.page = 0;
+  raw.loc = -1;
+  raw.krow = raw.vrow = 0u;
+  {
+    const int32_t key = d.k0 + lane;
+    int32_t idx;
+    if (p.pg.page_shift >= 0) {
+      idx = key >> p.pg.page_shift;
+      raw.off = key & (p.pg.page_size - 1);
+    } else {
+      idx = (int32_t)(((uint64_t)(uint32_t)key * p.pg.div_magic) >> p.pg.div_shift);
+      raw.off = key - idx * p.pg.page_size;
+    }
+    if (idx >= p.pg.table_width) raw.off = -1;
+    else raw.page = pt_row[idx];
+  }
+  const int32_t L = uniform(min(*len_at, p.max_seq_len));
+  if (kStore) {
+    raw.loc = *loc_at;
+    // (lane offset hidden from the compiler, as in the split path)
+    int32_t lo = 2 * lane;
+    asm volatile("" : "+v"(lo));
+    const int64_t e = ((int64_t)b * p.num_kv_heads + g) * kHeadDim;
+    raw.krow = *(const uint32_t*)(p.k_new + e + lo);
+    raw.vrow = *(const uint32_t*)(p.v_new + e + lo);
+  }
+  if (L <= 0) {
+    // No keys: the output row is not written (as in the split path). (The loads above
+    // are consumed on this path too, so that the compiler keeps them ahead of the
+    // length's wait.)
+    hold(raw.page);
+    hold(raw.krow);
+    return;
+  }
+  d.L = L;
   d.end = L;
   d.valid = d.k0 < L;
   d.last = 1;
@@ -563,8 +607,11 @@ void decode_small_kernel(DecodeKernelArgs p) {
   SoftmaxState st;
   reset_state(st);
   if (d.valid) {
-    const RawSlot raw = lookup_raw<kStore>(d, lane, p);
-    const int32_t slot = resolve(raw, p);
+    // Keys past L - 1 read key L - 1's slot (held by lane L - 1 - k0), as the clamped
+    // lookup of the split path does.
+    int32_t slot = resolve(raw, p);
+    const int32_t slot_last = __shfl(slot, min(L - 1 - d.k0, kBlock - 1));
+    if (d.k0 + lane >= L) slot = slot_last;
     if (kStore) store_new_row(d, raw, lane, p);
     Block blk;
     load_block<true, true>(blk, d, slot, n, grp, p);
