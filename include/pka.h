@@ -28,7 +28,10 @@
  * Data types. bf16 tensors are passed as `void*` (16-bit bf16 bit patterns);
  *   index arrays are int32; the softmax scale is a float.
  * Memory. Every pointer argument is a device pointer to contiguous row-major
- *   memory owned by the caller. The library allocates and frees nothing.
+ *   memory owned by the caller. The library allocates and frees nothing. bf16
+ *   tensors and workspaces start on a 16-byte boundary and int32 arrays on a 4-byte
+ *   one (every hipMalloc or torch allocation does); a call given a pointer that
+ *   does not returns PKA_E_UNSUPPORTED.
  * Pools. k_pool and v_pool are each [num_pages * page_size, Hkv, D] bf16: slot-major,
  *   one slot holds one token's K (or V) for all Hkv kv heads, and page p owns
  *   slots p*page_size .. p*page_size + page_size - 1.
@@ -237,9 +240,10 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
                            int32_t max_extend, int32_t max_seq_len, float scale, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pka_paged_attn_prefill needs: 4 bytes per (request, 256-row q
- * tile) item when batch > 1 (the launch orders its work heaviest first there), else 0.
- * Contents on entry are ignored; calls that run concurrently must not share it. */
+/* Workspace bytes pka_paged_attn_prefill needs: 16 bytes per (request, 256-row q
+ * tile) item when batch > 1 (the launch orders its work heaviest first there and
+ * keeps each item's request lengths beside it), else 0. Contents on entry are
+ * ignored; calls that run concurrently must not share it. */
 size_t pka_prefill_workspace_bytes(const pka_geom* geom, int32_t batch, int32_t num_tokens,
                                    int32_t max_extend);
 

@@ -28,6 +28,11 @@ int attn_geom_status(const pka_geom* g) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The kernels move bf16 rows and workspace entries in 16-byte vector accesses (and
+// copy pool rows straight into LDS in 16-byte pieces), and read index arrays as int32.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 int launch_status(hipError_t e) { return e == hipSuccess ? PKA_OK : PKA_E_HIP; }
 
 }  // namespace
@@ -60,6 +65,9 @@ int pka_store_kv(const pka_geom* geom, const void* k_new, const void* v_new,
   if (geom->head_dim % 8 != 0) return PKA_E_UNSUPPORTED;
   if (num_tokens == 0) return PKA_OK;
   if (!k_new || !v_new || !out_loc || !k_pool || !v_pool) return PKA_E_NULLPTR;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(out_loc))
+    return PKA_E_UNSUPPORTED;
   pka::StoreArgs a;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -110,6 +118,12 @@ int decode_impl(const pka_geom* geom, const void* q, const void* k_pool, const v
   if (page_table_stride < pages_needed) return PKA_E_SHAPE;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return PKA_E_NULLPTR;
   if (store && (!store->k_new || !store->v_new || !store->out_loc)) return PKA_E_NULLPTR;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || !aligned16(workspace))
+    return PKA_E_UNSUPPORTED;
+  if (store && (!aligned16(store->k_new) || !aligned16(store->v_new) ||
+                !aligned4(store->out_loc)))
+    return PKA_E_UNSUPPORTED;
   const pka::DecodePlan plan = pka::plan_decode(batch, geom->num_kv_heads, group, max_seq_len);
   const size_t need =
       pka::decode_workspace_bytes(batch, geom->num_q_heads, geom->num_kv_heads, plan);
@@ -216,6 +230,10 @@ int pka_paged_attn_prefill(const pka_geom* geom, const void* q, const void* k_po
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !prefix_lens || !extend_lens ||
       !cu_extend || !out)
     return PKA_E_NULLPTR;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || !aligned4(prefix_lens) ||
+      !aligned4(extend_lens) || !aligned4(cu_extend) || !aligned16(workspace))
+    return PKA_E_UNSUPPORTED;
   const size_t need = pka::prefill_workspace_bytes(batch, (int32_t)group, max_extend);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKA_E_WORKSPACE;
   pka::PrefillArgs a;

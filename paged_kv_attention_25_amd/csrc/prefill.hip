@@ -84,7 +84,9 @@ struct PrefillKernelArgs {
   int32_t group;
   int32_t tiles_per_seq;  // ceil(max_extend * G / 256)
   float scale_log2;
-  const int32_t* __restrict__ schedule;  // item order (heaviest first), or null
+  // Item order (heaviest first), or null: entry i = {item, prefix_lens[b],
+  // extend_lens[b], cu_extend[b]} of the i-th item to run (b = its request).
+  const i32x4* __restrict__ schedule;
 };
 
 // Work item r (0 .. tiles_per_seq*batch-1) is q tile tiles_per_seq-1 - r/batch of request
@@ -108,10 +110,13 @@ constexpr int kPlanBins = 4096;  // work beyond 4095 tiles shares the last bin
 // Dispatch order for several requests: one workgroup counting-sorts the work items by
 // their number of key tiles, heaviest first (longest-processing-time-first list
 // scheduling onto the CUs), so that long items do not start last and leave a tail.
-// The order of items with equal work is arbitrary; it only affects timing.
+// The order of items with equal work is arbitrary; it only affects timing. Each entry
+// carries its request's lengths and row offset, so a block gets all it needs to start
+// in one load.
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens,
-    int32_t batch, int32_t group, int32_t tiles_per_seq, int32_t* __restrict__ schedule) {
+    const int32_t* __restrict__ cu_extend, int32_t batch, int32_t group,
+    int32_t tiles_per_seq, i32x4* __restrict__ schedule) {
   __shared__ int32_t start[kPlanBins];  // histogram, then first position of each bin
   __shared__ int32_t wave_tot[kPlanThreads / 64];
   const int tid = threadIdx.x;
@@ -154,7 +159,8 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   for (int it = tid; it < items; it += kPlanThreads) {
     const int w = min(item_tiles(it, prefix_lens, extend_lens, batch, group, tiles_per_seq),
                       kPlanBins - 1);
-    schedule[atomicAdd(&start[w], 1)] = it;
+    const int b = it % batch;
+    schedule[atomicAdd(&start[w], 1)] = i32x4{it, prefix_lens[b], extend_lens[b], cu_extend[b]};
   }
 }
 
@@ -224,17 +230,27 @@ void prefill_kernel(PrefillKernelArgs p) {
   // together); the item comes from the schedule when there is one.
   const int id = blockIdx.x;
   const int g = id % p.num_kv_heads;
-  const int rest = p.schedule ? p.schedule[id / p.num_kv_heads] : id / p.num_kv_heads;
+  int rest, e, prefix, q_row0;
+  if (p.schedule) {
+    const i32x4 entry = p.schedule[id / p.num_kv_heads];
+    rest = entry[0];
+    prefix = entry[1];
+    e = entry[2];
+    q_row0 = entry[3];
+  } else {
+    rest = id / p.num_kv_heads;
+    const int b1 = rest % p.batch;
+    e = p.extend_lens[b1];
+    prefix = p.prefix_lens[b1];
+    q_row0 = p.cu_extend[b1];
+  }
   const int b = rest % p.batch;
   const int tile = p.tiles_per_seq - 1 - rest / p.batch;
 
-  const int e = p.extend_lens[b];
   const int G = p.group;
   const int nrows = e * G;
   const int row0 = tile * kRowsPerBlock;
   if (row0 >= nrows) return;
-  const int prefix = p.prefix_lens[b];
-  const int q_row0 = p.cu_extend[b];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -531,7 +547,7 @@ void prefill_kernel(PrefillKernelArgs p) {
 size_t prefill_workspace_bytes(int32_t batch, int32_t group, int32_t max_extend) {
   if (batch <= 1 || max_extend <= 0 || group <= 0) return 0;
   const int64_t tiles = ((int64_t)max_extend * group + kRowsPerBlock - 1) / kRowsPerBlock;
-  return (size_t)(tiles * batch) * sizeof(int32_t);
+  return (size_t)(tiles * batch) * sizeof(i32x4);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -557,9 +573,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   k.scale_log2 = a.scale * kLog2e;
   k.schedule = nullptr;
   if (prefill_workspace_bytes(a.batch, k.group, a.max_extend) > 0) {
-    int32_t* sched = (int32_t*)a.workspace;
+    i32x4* sched = (i32x4*)a.workspace;
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.prefix_lens,
-                       a.extend_lens, a.batch, k.group, k.tiles_per_seq, sched);
+                       a.extend_lens, a.cu_extend, a.batch, k.group, k.tiles_per_seq, sched);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     k.schedule = sched;

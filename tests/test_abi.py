@@ -87,11 +87,12 @@ def test_workspace_sizes(L):
     assert L.pka_decode_workspace_bytes(ctypes.byref(g3), 32, 32768) == \
         2 * 1023 * G * 129 * 4 + 33 * 4
     assert L.pka_decode_workspace_bytes(None, 4, 100) == 0
-    # prefill: one int32 per (request, 256-row q tile) item when batch > 1, else 0
+    # prefill: one 16-byte entry (item and its request's lengths) per (request, 256-row
+    # q tile) item when batch > 1, else 0
     assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 1, 10, 6) == 0
     g40 = geom(num_q_heads=40, num_kv_heads=8)                      # G = 5
-    assert L.pka_prefill_workspace_bytes(ctypes.byref(g40), 32, 8192, 700) == 4 * 32 * 14
-    assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 2, 10, 6) == 4 * 2 * 1
+    assert L.pka_prefill_workspace_bytes(ctypes.byref(g40), 32, 8192, 700) == 16 * 32 * 14
+    assert L.pka_prefill_workspace_bytes(ctypes.byref(g), 2, 10, 6) == 16 * 2 * 1
 
 
 def test_decode_argument_errors(L):
@@ -171,6 +172,7 @@ def test_prefill_argument_errors(L):
     # several requests need the dispatch-order workspace
     assert prefill(L, geom()) == pka.PKA_E_WORKSPACE
     assert prefill(L, geom(), ws=FAKE, ws_bytes=4) == pka.PKA_E_WORKSPACE
+    assert prefill(L, geom(), ws=FAKE, ws_bytes=15) == pka.PKA_E_WORKSPACE
     assert prefill(L, geom(), tokens=0) == pka.PKA_OK
     assert prefill(L, geom(), batch=0) == pka.PKA_OK
 
@@ -185,6 +187,26 @@ def test_store_argument_errors(L):
     assert st(g, kn=None) == pka.PKA_E_NULLPTR
     assert st(g, n=0) == pka.PKA_OK
     assert st(geom(num_pages=1 << 31)) == pka.PKA_E_SHAPE         # slots must fit int32
+
+
+def test_misaligned_pointers_are_rejected(L):
+    # bf16 tensors and workspaces on 16-byte boundaries, int32 arrays on 4-byte ones;
+    # rejected on the host, before anything is enqueued
+    odd16 = ctypes.c_void_p(0x1008)   # 8 bytes past a 16-byte boundary
+    odd4 = ctypes.c_void_p(0x1002)
+    g = geom()
+    assert prefill(L, g, q=odd16, ws=FAKE, ws_bytes=1 << 20) == pka.PKA_E_UNSUPPORTED
+    assert prefill(L, g, ws=odd16, ws_bytes=1 << 20) == pka.PKA_E_UNSUPPORTED
+    assert decode(L, g, q=odd16) == pka.PKA_E_UNSUPPORTED
+    assert decode(L, g, batch=32, max_seq=32768, stride=32768, ws=odd16,
+                  ws_bytes=1 << 26) == pka.PKA_E_UNSUPPORTED
+    assert decode_store(L, g, k_new=odd16) == pka.PKA_E_UNSUPPORTED
+    assert decode_store(L, g, out_loc=odd4) == pka.PKA_E_UNSUPPORTED
+    assert decode_store_noalloc(L, g, out=odd16) == pka.PKA_E_UNSUPPORTED
+    st = lambda kn=FAKE, loc=FAKE: L.pka_store_kv(ctypes.byref(g), kn, FAKE, loc, 4, FAKE, FAKE,
+                                                  None)
+    assert st(kn=odd16) == pka.PKA_E_UNSUPPORTED
+    assert st(loc=odd4) == pka.PKA_E_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
