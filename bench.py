@@ -246,6 +246,28 @@ def two_stream_step_us(runner, steps, warmup, flush):
     return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
+def prefill_alone_us(runner, idx, calls, warm_seconds):
+    """The prefill call of part `idx` alone at a settled shader clock: after
+    `warm_seconds` of continuous prefill calls, `calls` back-to-back calls between one
+    pair of events (no cache flush, no marker between calls); mean µs per call."""
+    import torch
+    for _ in range(5):
+        runner.attend(idx)
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < warm_seconds:
+        for _ in range(20):
+            runner.attend(idx)
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(calls):
+        runner.attend(idx)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / calls
+
+
 def _host_u16(t):
     return t.detach().cpu().contiguous().numpy().view(np.uint16)
 
@@ -674,6 +696,14 @@ def time_part(name, steps, warmup, flush, log, cpu=True, warm_seconds=PART_WARM_
             rec["prefill_frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
             rec["prefill_flops"] = prefill_flops(p, st)
             rec["prefill_GBs_context"] = round(prefill_bytes(p, st) / (us * 1e-6) / 1e9, 1)
+            # context: the same call alone, back to back, once the clock has settled
+            ua = prefill_alone_us(r, i, 50, max(warm_seconds, 0.5))
+            ta = prefill_flops(p, st) / (ua * 1e-6) / 1e12
+            rec["prefill_alone"] = {
+                "us": round(ua, 2), "TFLOPs": round(ta, 1),
+                "frac_mfma": round(ta / MFMA_BF16_PEAK_TFLOPS, 4),
+                "how": "the prefill call alone: 50 back-to-back calls after half a second "
+                       "of continuous prefill work, no cache flush, one event pair"}
     if r.fused:
         rec["unfused_step_us"] = round(tot_u * 1e3, 2)   # store_kv, then decode
     if name == "tiny_decode":
