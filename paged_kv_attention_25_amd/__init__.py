@@ -181,7 +181,7 @@ def _types():
 def _tensor(t, name, kind, shape):
     """`t` must be a contiguous torch tensor of `kind` ("bf16": bfloat16 or 16-bit
     integer bit patterns; "i32"; "bytes": any dtype) whose shape matches `shape`
-    (None entries match any size)."""
+    (None entries match any size), starting on a 16-byte boundary (4 for "i32")."""
     tensor_t, bf16_dtypes, i32 = _types()
     if not isinstance(t, tensor_t):
         raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
@@ -204,6 +204,12 @@ def _tensor(t, name, kind, shape):
             raise ValueError(f"{name} has shape {list(got)}, expected {want}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    # The kernels read index arrays as int32 and move bf16 rows and workspace entries in
+    # 16-byte pieces; the library rejects other starts too, with a less specific status.
+    align = 4 if kind == "i32" else 16
+    if t.numel() > 0 and t.data_ptr() % align:
+        raise ValueError(f"{name} must start on a {align}-byte boundary "
+                         f"(a view into another tensor may not)")
 
 
 def _same_gpu(named):

@@ -117,6 +117,26 @@ def test_prefill_rejections():
     expect(pka.paged_attn_prefill, {**a, "workspace": [0]}, "workspace must be a torch.Tensor")
 
 
+def misaligned_bf16(*shape, shift=1):
+    """A contiguous bf16 view starting `shift` elements (2*shift bytes) into its storage."""
+    n = int(np.prod(shape))
+    return bf16(n + 8)[shift:shift + n].view(*shape)
+
+
+def test_misaligned_views_are_rejected():
+    a = decode_args()
+    expect(pka.paged_attn_decode, {**a, "q": misaligned_bf16(3, HQ, D)}, "16-byte boundary")
+    expect(pka.paged_attn_decode, {**a, "q": misaligned_bf16(3, HQ, D, shift=4)},
+           "16-byte boundary")
+    # 8 elements = 16 bytes in: aligned, so the call goes on to the device check
+    expect(pka.paged_attn_decode, {**a, "q": misaligned_bf16(3, HQ, D, shift=8)}, "on the GPU")
+    s = store_args()
+    expect(pka.store_kv, {**s, "k_new": misaligned_bf16(3, HKV, D)}, "k_new must start")
+    p = prefill_args()
+    ws = torch.zeros(1 << 12, dtype=torch.uint8)[3:]
+    expect(pka.paged_attn_prefill, {**p, "workspace": ws}, "workspace must start")
+
+
 # --- debug-mode metadata checks (checks.py) ------------------------------------------------
 
 def test_out_loc_checks():
